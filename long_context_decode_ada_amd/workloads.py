@@ -1,0 +1,273 @@
+"""Seeded synthetic decode workloads (inputs only).
+
+This module builds the inputs that both the HIP path and the CPU oracle
+consume: keys, values, queries, sequence lengths, block tables, page tiers and
+page offsets.  It holds none of the method's arithmetic (no angles, no
+quantisers, no attention); it only draws random numbers and lays out pages.
+
+Shapes and distributions follow the workloads of the page "SPHERICAL KV:
+Angle-Domain Attention and Rate-Distortion Retention for Efficient
+Long-Context Inference" (section 4: Llama-3.1-8B-class models, contexts of
+8K/32K/128K on a paged, ragged serving substrate, section 2.3).  The models
+and datasets of that section are not used: seeded synthetic tensors of the
+same shapes stand in for them.
+
+Workloads (sizes at scale 1):
+  tiny        B=1, 1/1 heads, d=64, T=256 (16 pages), b=4, uniform radius,
+              identity block table, keys/query/values N(0,1)
+  gqa_t32k    B=8, 32/8 heads, d=128, T=32768, b=4, log radius, keys
+              N(0, diag(s^2)) with s ~ LogNormal(0, 0.5) per (kv head, dim),
+              RoPE (theta 5e5) at positions 0..T-1, query N(0,1) with RoPE at
+              T, values bf16 N(0,1), physical pages shuffled
+  long_t128k  B=1, 32/8, d=128, T=131072, b=3, log radius, as gqa_t32k
+  ragged_b64  B=64, 32/8, d=128, lengths floor(LogNormal(ln 8192, 1))
+              clipped to [512, 65536], b=4, log radius, shared pool of
+              ceil(1.25 * pages) physical pages assigned at random
+  mixed_tiers gqa_t32k shapes; logical page 0 (the 4 sink tokens and the
+              rest of their page) at b=8; every other page draws b from
+              {2,4,6,8} with p={.3,.4,.2,.1}; 1023 of the 2047 non-sink pages
+              per sequence are evicted (absent from the block table);
+              variable-size pages addressed through page_off
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+SEED = 20260609
+PAGE = 16
+UNIFORM, LOG = 0, 1
+ROPE_THETA = 500000.0
+
+NAMES = ("tiny", "gqa_t32k", "long_t128k", "ragged_b64", "mixed_tiers")
+
+
+def record_bytes(d: int, b: int) -> int:
+    """Bytes of one key record in the pool layout (16-byte multiple)."""
+    return 16 * (((d - 1) * b + 127) // 128)
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    d: int
+    hq: int
+    hkv: int
+    B: int
+    radius_mode: int
+    tier_mask: int
+    seq_lens: np.ndarray            # int32 [B] resident tokens
+    block_table: np.ndarray         # int32 [B][max_pages]
+    num_pages: int
+    page_bits: np.ndarray           # uint8 [num_pages]
+    page_off: Optional[np.ndarray]  # uint64 [num_pages] or None
+    bstride: int                    # tier used for the fixed page stride when page_off is None
+    kcode_bytes: int
+    keys: np.ndarray                # float32 [n][hkv][d]
+    values: np.ndarray              # uint16 (bf16 bits) [n][hkv][d]
+    slot: np.ndarray                # int64 [n] = phys*16 + token-in-page
+    q: np.ndarray                   # float32 [B][hq][d]
+    scale: float = 0.0              # 0 => 1/sqrt(d)
+    seed: int = SEED
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum())
+
+    def bytes_per_step(self) -> int:
+        """Algorithmic HBM bytes of one decode step: per resident (token, kv
+        head) one record, one radius byte and d bf16 values; per resident
+        (page, kv head) one block-table entry and one page header byte
+        (plus 8 offset bytes when page_off is used); the query and output."""
+        tot = 0
+        for s in range(self.B):
+            n = int(self.seq_lens[s])
+            npg = (n + PAGE - 1) // PAGE
+            for p in range(npg):
+                phys = int(self.block_table[s, p])
+                ntok = min(PAGE, n - p * PAGE)
+                b = int(self.page_bits[phys])
+                tot += self.hkv * ntok * (record_bytes(self.d, b) + 1 + 2 * self.d)
+                tot += self.hkv * (4 + 1 + (8 if self.page_off is not None else 0))
+        tot += self.B * self.hq * self.d * 4 * 2
+        return tot
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def _rope(x: np.ndarray, pos: np.ndarray, d: int) -> np.ndarray:
+    """Rotate-half RoPE of x [..., n, h, d] at positions pos [n]."""
+    half = d // 2
+    inv = ROPE_THETA ** (-np.arange(half, dtype=np.float64) * 2.0 / d)
+    ang = pos.astype(np.float64)[:, None] * inv[None, :]
+    c = np.cos(ang).astype(np.float32)[:, None, :]
+    s = np.sin(ang).astype(np.float32)[:, None, :]
+    x1 = x[..., :half]
+    x2 = x[..., half:]
+    out = np.empty_like(x)
+    out[..., :half] = x1 * c - x2 * s
+    out[..., half:] = x2 * c + x1 * s
+    return out
+
+
+def _streams(idx: int, n: int = 10):
+    ss = np.random.SeedSequence(SEED).spawn(len(NAMES))[idx]
+    return [np.random.default_rng(c) for c in ss.spawn(n)]
+
+
+def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool = True) -> Workload:
+    """Build one workload.  ``scale`` < 1 shrinks the context (and, for
+    ragged_b64, the lengths) for oracle-sized tests; ``batch`` overrides B;
+    ``data=False`` builds the page structure only (empty keys/values/query).
+    Every part draws from its own seeded stream, so the structure does not
+    depend on ``data``."""
+    if name not in NAMES:
+        raise KeyError(name)
+    idx = NAMES.index(name)
+    r_keys, r_vals, r_q, r_len, r_pages, r_tier, r_evict, r_scale, _, _ = _streams(idx)
+
+    if name == "tiny":
+        d, hq, hkv, B, T = 64, 1, 1, 1, 256
+        B = batch or B
+        T = max(PAGE, int(T * scale))
+        lens = np.full(B, T, np.int32)
+        mode, tiers = UNIFORM, {4}
+    elif name in ("gqa_t32k", "long_t128k", "mixed_tiers"):
+        d, hq, hkv = 128, 32, 8
+        B = {"gqa_t32k": 8, "long_t128k": 1, "mixed_tiers": 8}[name]
+        T = {"gqa_t32k": 32768, "long_t128k": 131072, "mixed_tiers": 32768}[name]
+        B = batch or B
+        T = max(2 * PAGE, int(T * scale))
+        lens = np.full(B, T, np.int32)
+        mode = LOG
+        tiers = {"gqa_t32k": {4}, "long_t128k": {3}, "mixed_tiers": {2, 4, 6, 8}}[name]
+    else:  # ragged_b64
+        d, hq, hkv, B = 128, 32, 8, 64
+        B = batch or B
+        raw = np.floor(r_len.lognormal(np.log(8192.0), 1.0, size=B))
+        lens = np.clip(raw, 512, 65536)
+        lens = np.maximum(np.floor(lens * scale), 1).astype(np.int32)
+        mode, tiers = LOG, {4}
+
+    # ---- logical pages, tiers, eviction (positions of resident tokens) ----
+    pos_list, tier_list = [], []
+    for s in range(B):
+        if name == "mixed_tiers":
+            T = int(lens[s])
+            npg = (T + PAGE - 1) // PAGE
+            tier = r_tier.choice(np.array([2, 4, 6, 8]), size=npg, p=[0.3, 0.4, 0.2, 0.1])
+            tier[0] = 8                                   # sink page: protected, b_max
+            nonsink = np.arange(1, npg)
+            evict = r_evict.choice(nonsink, size=len(nonsink) // 2, replace=False)
+            keep = np.setdiff1d(np.arange(npg), evict)    # sorted: logical order kept
+            pos = np.concatenate([np.arange(p * PAGE, min((p + 1) * PAGE, T)) for p in keep])
+            tier_list.append(tier[keep].astype(np.uint8))
+            lens[s] = len(pos)
+            pos_list.append(pos)
+        else:
+            n = int(lens[s])
+            npg = (n + PAGE - 1) // PAGE
+            pos_list.append(np.arange(n))
+            tier_list.append(np.full(npg, next(iter(tiers)), np.uint8))
+    lens = np.asarray(lens, np.int32)
+    npages = [(int(n) + PAGE - 1) // PAGE for n in lens]
+    total_pages = int(sum(npages))
+    max_pages = max(npages) if npages else 1
+
+    # ---- physical placement ----
+    if name == "tiny":
+        num_pages = total_pages
+        perm = np.arange(num_pages)
+    elif name == "ragged_b64":
+        num_pages = int(np.ceil(1.25 * total_pages))
+        perm = r_pages.permutation(num_pages)[:total_pages]
+    else:
+        num_pages = total_pages
+        perm = r_pages.permutation(num_pages)
+    block_table = np.zeros((B, max_pages), np.int32)
+    page_bits = np.full(num_pages, max(tiers), np.uint8)
+    k = 0
+    for s in range(B):
+        block_table[s, : npages[s]] = perm[k: k + npages[s]]
+        page_bits[perm[k: k + npages[s]]] = tier_list[s]
+        k += npages[s]
+    if len(tiers) > 1:
+        sizes = hkv * PAGE * np.array([record_bytes(d, int(b)) for b in page_bits], np.uint64)
+        page_off = np.zeros(num_pages, np.uint64)
+        page_off[1:] = np.cumsum(sizes)[:-1]
+        kcode_bytes = int(sizes.sum())
+        bstride = max(tiers)
+    else:
+        page_off = None
+        bstride = max(tiers)
+        kcode_bytes = num_pages * hkv * PAGE * record_bytes(d, bstride)
+
+    # ---- keys, values, query ----
+    n_tok = int(lens.astype(np.int64).sum())
+    if not data:
+        keys = np.zeros((0, hkv, d), np.float32)
+        q = np.zeros((B, hq, d), np.float32)
+    elif name == "tiny":
+        keys = r_keys.standard_normal((n_tok, hkv, d), dtype=np.float32)
+        q = r_q.standard_normal((B, hq, d), dtype=np.float32)
+    else:
+        chan = r_scale.lognormal(0.0, 0.5, size=(hkv, d)).astype(np.float32)
+        keys = np.empty((n_tok, hkv, d), np.float32)
+        q = np.empty((B, hq, d), np.float32)
+        o = 0
+        for s in range(B):
+            n = int(lens[s])
+            z = r_keys.standard_normal((n, hkv, d), dtype=np.float32)
+            keys[o: o + n] = _rope(z * chan[None], pos_list[s], d)
+            qpos = (int(pos_list[s][-1]) + 1) if n else 0
+            qs = r_q.standard_normal((1, hq, d), dtype=np.float32)
+            q[s] = _rope(qs, np.array([qpos]), d)[0]
+            o += n
+    if data:
+        values = _bf16_bits(r_vals.standard_normal((n_tok, hkv, d), dtype=np.float32))
+    else:
+        values = np.zeros((0, hkv, d), np.uint16)
+
+    slot = np.empty(n_tok, np.int64)
+    o = 0
+    for s in range(B):
+        n = int(lens[s])
+        t = np.arange(n)
+        slot[o: o + n] = block_table[s, t // PAGE].astype(np.int64) * PAGE + t % PAGE
+        o += n
+
+    return Workload(name=name, d=d, hq=hq, hkv=hkv, B=B, radius_mode=mode,
+                    tier_mask=sum(1 << b for b in tiers), seq_lens=lens,
+                    block_table=block_table, num_pages=num_pages, page_bits=page_bits,
+                    page_off=page_off, bstride=bstride, kcode_bytes=kcode_bytes,
+                    keys=keys, values=values, slot=slot, q=q)
+
+
+def host_pools(w: Workload, poison: bool = True) -> dict:
+    """Host arrays in the pool layout, filled with poison (0xFF bytes, bf16
+    NaN) so that a reader of an unwritten byte is caught."""
+    fill8 = 0xFF if poison else 0
+    return {
+        "d": w.d, "hkv": w.hkv, "bstride": w.bstride,
+        "page_bits": w.page_bits, "page_off": w.page_off,
+        "kcode": np.full(w.kcode_bytes, fill8, np.uint8),
+        "rcode": np.full(w.num_pages * w.hkv * PAGE, fill8, np.uint8),
+        "v": np.full(w.num_pages * w.hkv * w.d * PAGE, 0x7FC0 if poison else 0, np.uint16),
+    }
+
+
+def token_keys(w: Workload, s: int) -> slice:
+    """Rows of ``keys``/``values``/``slot`` that belong to sequence s."""
+    start = int(w.seq_lens[:s].astype(np.int64).sum())
+    return slice(start, start + int(w.seq_lens[s]))

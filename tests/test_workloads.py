@@ -1,0 +1,68 @@
+"""Synthetic workload generator: determinism and structure (CPU only)."""
+import numpy as np
+import pytest
+
+from long_context_decode_ada_amd import workloads as W
+from oracle import oracle as O
+
+
+@pytest.mark.parametrize("name,scale", [("tiny", 1.0), ("gqa_t32k", 1 / 256), ("long_t128k", 1 / 1024),
+                                        ("ragged_b64", 1 / 64), ("mixed_tiers", 1 / 128)])
+def test_same_seed_same_bytes(name, scale):
+    a = W.make(name, scale)
+    b = W.make(name, scale)
+    for f in ("keys", "values", "q", "slot", "block_table", "seq_lens", "page_bits"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    # every resident slot is distinct and inside the pool
+    assert len(np.unique(a.slot)) == len(a.slot)
+    assert a.slot.max() < a.num_pages * W.PAGE
+    assert a.keys.shape == (a.n_tokens, a.hkv, a.d)
+    c = W.make(name, scale, data=False)
+    for f in ("slot", "block_table", "seq_lens", "page_bits"):
+        assert np.array_equal(getattr(a, f), getattr(c, f)), f
+
+
+def test_ragged_lengths_follow_the_recipe():
+    w = W.make("ragged_b64", data=False)
+    assert w.B == 64 and w.seq_lens.min() >= 512 and w.seq_lens.max() <= 65536
+    npg = ((w.seq_lens + 15) // 16).sum()
+    assert w.num_pages == int(np.ceil(1.25 * npg))
+    used = np.concatenate([w.block_table[s, : (w.seq_lens[s] + 15) // 16] for s in range(w.B)])
+    assert len(np.unique(used)) == len(used)
+
+
+def test_mixed_tiers_structure():
+    w = W.make("mixed_tiers", scale=1 / 16)   # T = 2048: 128 logical pages per sequence
+    npg_logical = 2048 // 16
+    resident_pages = (w.seq_lens + 15) // 16
+    assert np.all(resident_pages == npg_logical - (npg_logical - 1) // 2)
+    for s in range(w.B):
+        assert w.page_bits[w.block_table[s, 0]] == 8         # sink page at b_max
+    assert set(np.unique(w.page_bits)) <= {2, 4, 6, 8}
+    sizes = [w.hkv * 16 * W.record_bytes(w.d, int(b)) for b in w.page_bits]
+    assert np.array_equal(w.page_off[1:], np.cumsum(sizes)[:-1])
+
+
+def test_full_size_shapes_are_the_stated_ones():
+    # sizes only (no key generation): the headline workload
+    w = W.make("tiny")
+    assert (w.B, w.hq, w.hkv, w.d, int(w.seq_lens[0])) == (1, 1, 1, 64, 256)
+    assert w.num_pages == 16 and np.array_equal(w.block_table[0], np.arange(16))
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.1415927], np.float32)
+    h = W._bf16_bits(x)
+    back = (h.astype(np.uint32) << 16).view(np.float32)
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.015625 and back[3] == -2.5
+    assert abs(back[4] - 3.140625) < 1e-7
+
+
+def test_small_workloads_run_through_the_oracle():
+    for name, scale in (("tiny", 1.0), ("mixed_tiers", 1 / 256)):
+        w = W.make(name, scale, batch=2)
+        pools = W.host_pools(w)
+        rg = O.calibrate(w.keys)
+        O.encode(pools, w.keys, w.values, w.slot, w.radius_mode, rg)
+        out = O.decode(pools, w.radius_mode, rg, w.q, w.block_table, w.seq_lens)
+        assert np.isfinite(out).all()
