@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""ADA paged-decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa_t32k]
+
+One step is one ska_decode_attention call over the whole batch: query
+preparation, the paged decode kernel (logits from angle codes, online softmax,
+bf16 value accumulation) and the split merge.  Inputs are resident in HBM
+before the timed region; two copies of the page pools are alternated so that
+the 256 MB Infinity Cache cannot serve one step's pages to the next.
+
+Prints one JSON line (stdout): effective HBM GB/s on algorithmic bytes (the
+compressed bytes the method must read), KV tokens/s, the decode kernel's
+roofline figures and the CPU oracle's throughput on a bounded sample.
+Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["long_context_decode_ada_amd/csrc/k_decode.hip", "long_context_decode_ada_amd/csrc/ska_internal.h"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def decode_kernel_bytes(w) -> int:
+    """Algorithmic bytes the decode kernel must read in one launch: per
+    resident (token, kv head) the record, the radius byte and d bf16 values;
+    per resident (page, kv head) the block-table entry and the page header
+    (and the 8-byte page offset when pages have variable size)."""
+    return w.bytes_per_step() - w.B * w.hq * w.d * 4 * 2
+
+
+def read_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, "k_decode_%s_pmc.md" % workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and " = " in line:
+            k, v = line[2:].split(" = ", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, nseq: int):
+    """The CPU oracle (plain fp64 C, all host threads) on the first `nseq`
+    sequences of the workload: encode untimed, decode timed."""
+    import numpy as np
+    from long_context_decode_ada_amd import workloads as W
+    from oracle import oracle as O
+    rng = O.calibrate(w.keys)
+    pools = W.host_pools(w, poison=False)
+    rows = slice(0, int(w.seq_lens[:nseq].astype(np.int64).sum()))
+    O.encode(pools, w.keys[rows], w.values[rows], w.slot[rows], w.radius_mode, rng)
+    pairs = [(s, h) for s in range(nseq) for h in range(w.hq)]
+    t0 = time.perf_counter()
+    O.decode(pools, w.radius_mode, rng, w.q, w.block_table, w.seq_lens, pairs=pairs)
+    dt = time.perf_counter() - t0
+    ntok = int(w.seq_lens[:nseq].sum())
+    per_tok = W.record_bytes(w.d, int(w.page_bits[w.block_table[0, 0]])) + 1 + 2 * w.d
+    npg = sum((int(w.seq_lens[s]) + 15) // 16 for s in range(nseq))
+    nbytes = ntok * w.hkv * per_tok + npg * w.hkv * 5
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": O.max_threads(), "kind": "oracle",
+            "kv_tokens_per_s": ntok / dt, "seconds": dt,
+            "sample": "%d of %d sequences of %s (%d tokens, all %d query heads), decode only" %
+                      (nseq, w.B, w.name, ntok, w.hq)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa_t32k")
+    ap.add_argument("--copies", type=int, default=2, help="pool copies alternated across steps")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run a plain copy kernel of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the decode needs no inter-GPU "
+              "communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from long_context_decode_ada_amd import ska
+    from long_context_decode_ada_amd import workloads as W
+
+    t0 = time.time()
+    w = W.make(args.workload)
+    log("workload %s: B=%d hq=%d hkv=%d d=%d tokens=%d pages=%d (%.1fs)" %
+        (w.name, w.B, w.hq, w.hkv, w.d, w.n_tokens, w.num_pages, time.time() - t0))
+    dev = "cuda"
+    keys = torch.from_numpy(w.keys).to(dev)
+    vals = torch.from_numpy(w.values.view(np.int16)).to(dev)
+    slot = torch.from_numpy(w.slot).to(dev)
+    caches, rng = [], None
+    for c in range(args.copies):
+        pools = ska.DevicePools.for_workload(w, device=dev, poison=False)
+        cache = ska.Cache(pools)
+        ska.encode_keys(cache, keys, vals, slot, radius_range=rng)
+        rng = ska.radius_range(cache)
+        caches.append(cache)
+    del keys, vals, slot
+    torch.cuda.synchronize()
+    log("encoded %d pool copies (%.1fs)" % (args.copies, time.time() - t0))
+    q = torch.from_numpy(w.q).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    out = torch.empty((w.B, w.hq, w.d), dtype=torch.float32, device=dev)
+    nc = len(caches)
+
+    for i in range(args.warmup):
+        ska.decode_attention(caches[i % nc], q, bt, sl, num_splits=args.splits, out=out)
+    torch.cuda.synchronize()
+    for c in caches:
+        ska.profile_begin(c, args.steps)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        ska.decode_attention(caches[i % nc], q, bt, sl, num_splits=args.splits, out=out)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    prof = np.concatenate([ska.profile_read(c, args.steps) for c in caches])
+    for c in caches:
+        ska.profile_begin(c, 0)
+    k_ms = [float(x) for x in prof.mean(axis=0)]
+    log("timed %d steps: %.2f us/step; kernels qprep %.2f decode %.2f merge %.2f us" %
+        (args.steps, ms_per_step * 1e3, k_ms[0] * 1e3, k_ms[1] * 1e3, k_ms[2] * 1e3))
+    if not np.isfinite(out.cpu().numpy()).all():
+        log("non-finite output")
+        sys.exit(1)
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("copy kernel: %d MiB read + %d MiB written, 3 launches" % (args.copy_calib_mib, args.copy_calib_mib))
+
+    step_bytes = w.bytes_per_step()
+    ms_per_step = float(ms_per_step)
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kb = decode_kernel_bytes(w)
+    ach = float(kb / (k_ms[1] * 1e-3) / 1e9)
+    traffic = read_traffic(w.name)
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": "k_decode<d=%d,G=%d>" % (w.d, w.hq // w.hkv), "kernel_us": round(k_ms[1] * 1e3, 2),
+            "alg_bytes_per_launch": int(kb)}
+
+    cpu = None
+    if args.cpu_seqs > 0:
+        log("timing the CPU oracle on %d sequences" % args.cpu_seqs)
+        cpu = cpu_baseline(w, min(args.cpu_seqs, w.B))
+        log("oracle: %.3f GB/s (%.1fs, %d threads)" % (cpu["value"], cpu["seconds"], cpu["cores"]))
+
+    tiers = sorted({int(b) for b in np.unique(w.page_bits)})
+    line = {
+        "metric": "ADA decode effective HBM GB/s (% of peak) and KV tokens/s at T=32k",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "kv_tokens_per_s": round(w.n_tokens / (ms_per_step * 1e-3), 1),
+        "token_kvhead_per_s": round(w.n_tokens * w.hkv / (ms_per_step * 1e-3), 1),
+        "alg_bytes_per_step": int(step_bytes),
+        "config": {"workload": w.name, "B": w.B, "hq": w.hq, "hkv": w.hkv, "d": w.d,
+                   "T": int(w.seq_lens.max()), "angle_bits": tiers, "radius": "8-bit " +
+                   ("log" if w.radius_mode == W.LOG else "uniform"), "page": 16,
+                   "values": "bf16", "pool_copies": nc, "splits": args.splits or "auto"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

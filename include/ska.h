@@ -1,0 +1,167 @@
+/*
+ * ska.h -- C ABI of the Angle-Domain Attention (ADA) paged-decode library
+ * for AMD MI355X (gfx950).
+ *
+ * Method: the technical summary in the page "SPHERICAL KV: Angle-Domain
+ * Attention and Rate-Distortion Retention for Efficient Long-Context
+ * Inference" (gist.science summary of arXiv 2605.18856).
+ *   section 2.1  keys are split into a radius r = |k| and directional angles
+ *                phi = Phi(k/|k|); the cache stores a quantised radius r~ and
+ *                packed angle codes c; the decode kernel computes the logit
+ *                |q| * r~ * f_b(c_q, c_k) from the codes, f_b a cosine
+ *                similarity; no dense key is ever written to HBM.
+ *   section 2.2  pages are tier-homogeneous (one bit width b per page) and
+ *                read by header-guided streaming.
+ *   section 2.3  dense keys are mapped to spherical codes and stored in a
+ *                paged (vLLM-style) compressed store that the decode kernel
+ *                consumes directly.
+ *
+ * Format (the pages leave it open; fixed here):
+ *   Phi      hyperspherical coordinates: d-2 polar angles in [0, pi] and one
+ *            azimuth in [0, 2*pi); suffix sums of squares in binary64,
+ *            summed from the last component backwards.
+ *   angles   b uniform bins over each angle's range, code = bin index,
+ *            decided by binary64 predicates on squared quantities (ties to
+ *            the upper bin); decoded at bin centres.
+ *   radius   8 bits; uniform levels j*R_hi/255 or log-spaced levels over
+ *            [R_lo, R_hi], rounded at the (linear or log) midpoint.
+ *   record   KB(b) = 16*ceil((d-1)*b/128) bytes per key, four equal slices;
+ *            slice s holds angles [s*d/4, (s+1)*d/4) LSB-first, rest zero.
+ *   pools    page_bits[phys] (uint8)        tier b of the page
+ *            kcode + base(phys)             [Hkv][16][KB(b)] records,
+ *                                           base = page_off[phys] or
+ *                                           phys*Hkv*16*KB(b_max of mask)
+ *            rcode[phys][Hkv][16] (uint8)   radius codes
+ *            v[phys][Hkv][d][16]  (bf16)    values, dimension-major in a page
+ *            A slot is phys*16 + token-in-page.
+ *
+ * Memory: every pointer argument marked "device" is caller-owned device
+ * memory (any allocator; PyTorch in the tests).  The library owns only what
+ * it allocates inside a ska_cache (code tables, radius tables, the decode
+ * workspace) and frees it in ska_free.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the null stream).  All work is
+ * enqueued asynchronously on it.  The only host synchronisation is the
+ * calibrating ska_encode_keys call (it reads the radius range back).
+ *
+ * Errors: arguments are checked on the host before any HIP call; a bad one
+ * returns SKA_ERR_INVALID (or SKA_ERR_UNSUPPORTED for a legal but unbuilt
+ * shape) with nothing enqueued.  Launch failures return SKA_ERR_HIP.  Pages
+ * whose id or header is out of range are skipped by the kernels and flagged
+ * in a device error word (ska_device_errors).  No C++ exception crosses this
+ * ABI.  Calls on one ska_cache are not thread-safe.
+ */
+#ifndef SKA_H
+#define SKA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SKA_OK = 0,
+    SKA_ERR_INVALID = 1,
+    SKA_ERR_UNSUPPORTED = 2,
+    SKA_ERR_HIP = 3,
+    SKA_ERR_NOMEM = 4
+} ska_status;
+
+enum { SKA_RADIUS_UNIFORM = 0, SKA_RADIUS_LOG = 1 };
+enum { SKA_Q_CODED = 0, SKA_Q_EXACT = 1 };
+enum { SKA_PAGE_SIZE = 16 };
+
+/* Device error flags (ska_device_errors). */
+enum {
+    SKA_DEVERR_SLOT = 1u,     /* encode: slot outside the pool */
+    SKA_DEVERR_PAGE = 2u,     /* decode: block-table entry outside the pool */
+    SKA_DEVERR_TIER = 4u      /* page_bits value not in tier_mask */
+};
+
+typedef struct ska_cache ska_cache; /* opaque, library-owned */
+
+/* Caller-owned device pools (see the format above). */
+typedef struct {
+    int d;                    /* head dimension: 64 or 128 */
+    int num_kv_heads;         /* Hkv >= 1 */
+    int page_size;            /* must be 16 */
+    int64_t num_pages;        /* physical pages in the pool */
+    int radius_mode;          /* SKA_RADIUS_UNIFORM or SKA_RADIUS_LOG */
+    int radius_bits;          /* must be 8 */
+    uint32_t tier_mask;       /* bit b set => pages of b-bit angles allowed, b in {2,3,4,6,8} */
+    int query_mode;           /* SKA_Q_CODED: query angle-coded at each page's tier (f_b of two
+                                 codes); SKA_Q_EXACT: exact query direction */
+    uint8_t *kcode;           /* device: code records */
+    const uint64_t *page_off; /* device [num_pages] byte offsets (multiples of 16) or NULL */
+    uint8_t *rcode;           /* device: [num_pages][Hkv][16] */
+    uint16_t *v;              /* device: bf16 [num_pages][Hkv][d][16] */
+    const uint8_t *page_bits; /* device: [num_pages] */
+} ska_pool_desc;
+
+/* ska_encode_keys -- the write path of section 2.3: map dense keys to
+ * spherical codes (section 2.1) and store them, with their values, in the
+ * paged pools.
+ *   cache   in/out.  *cache == NULL creates a cache for `pool`; otherwise the
+ *           pool must have the same shape fields as at creation.
+ *   keys    device fp32 [n][Hkv][d]
+ *   values  device bf16 [n][Hkv][d] or NULL (values not written)
+ *   slot    device int64 [n]: phys*16 + token-in-page for each key
+ *   radius_range  host [Hkv][2] = (R_lo, R_hi) or NULL.  On creation with
+ *           NULL the range is calibrated per KV head over these keys
+ *           (R_hi = max |k|, R_lo = min positive |k|); this synchronises.
+ *           Ignored when the cache already exists.
+ * Each key is encoded at the tier page_bits[slot/16].  Returns SKA_OK. */
+ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool,
+                           const float *keys, const uint16_t *values,
+                           const int64_t *slot, int64_t n,
+                           const double *radius_range, void *stream);
+
+/* ska_decode_attention -- one ADA decode step over a page table (section 2.1
+ * logit estimator, section 2.2 header-guided page streaming): for sequence s
+ * and query head h (KV head h / (Hq/Hkv)), the logits
+ *     l_t = scale * |q| * r~_t * f_b(c_q, c_t)
+ * over the seq_lens[s] resident tokens (token t at page t/16 of row s of
+ * the block table, slot t%16), then softmax and the value-weighted sum.
+ *   q            device fp32 [batch][num_q_heads][d]
+ *   block_table  device int32 [batch][max_pages]
+ *   seq_lens     device int32 [batch] (0 gives a zero output row)
+ *   scale        softmax scale; 0 means 1/sqrt(d)
+ *   num_splits   page splits per sequence (split-T); 0 chooses
+ *   out          device fp32 [batch][num_q_heads][d]
+ *   logits_dbg   device fp32 [batch][num_q_heads][max_pages*16] or NULL;
+ *                receives l_t (natural units) at each resident position
+ * Hq/Hkv must be 1, 2 or 4.  Returns SKA_OK. */
+ska_status ska_decode_attention(ska_cache *cache, const float *q, int batch, int num_q_heads,
+                                const int32_t *block_table, int max_pages,
+                                const int32_t *seq_lens, float scale, int num_splits,
+                                float *out, float *logits_dbg, void *stream);
+
+/* The radius range in use (host [Hkv][2] = (R_lo, R_hi)). */
+ska_status ska_get_radius_range(const ska_cache *cache, double *range_out);
+
+/* OR of the device error flags raised since the last call, then cleared.
+ * Synchronises `stream`. */
+ska_status ska_device_errors(ska_cache *cache, void *stream, uint32_t *flags_out);
+
+/* Kernel timing for the measurement of section 3 of the page (HBM traffic
+ * and kernel-realised throughput on the paged substrate) and section 4
+ * ("kernel-realised efficiency"): ska_profile_begin makes the next
+ * `max_calls` ska_decode_attention calls on this cache record HIP events on
+ * their stream around each of their kernels (query preparation, decode,
+ * split merge); 0 stops recording.  ska_profile_read waits for the recorded
+ * events and writes ms_out[i*3 + k] for call i and kernel k, *n_out = calls
+ * recorded (at most max_calls). */
+ska_status ska_profile_begin(ska_cache *cache, int max_calls);
+ska_status ska_profile_read(ska_cache *cache, float *ms_out, int max_calls, int *n_out);
+
+/* Release everything the cache owns.  Accepts NULL. */
+void ska_free(ska_cache *cache);
+
+const char *ska_status_string(ska_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKA_H */

@@ -1,0 +1,480 @@
+// ska_api.cpp -- host side of the C ABI declared in include/ska.h:
+// argument validation, code and radius tables, the cache handle and its
+// workspace, split policy and kernel launches.
+//
+// Method: "SPHERICAL KV: Angle-Domain Attention and Rate-Distortion
+// Retention for Efficient Long-Context Inference", technical summary,
+// sections 2.1 (spherical codes, logit from codes), 2.2 (tier-homogeneous
+// pages) and 2.3 (encode into a paged store; decode consumes the codes).
+//
+// Host constants that enter integer decisions (angle bin edges, radius
+// edges) are computed here in binary64 with the C library's cos, sin, exp,
+// log and sqrt, built with -fno-builtin -ffp-contract=off so that each is the
+// library call and each product is rounded as written.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/ska.h"
+#include "ska_internal.h"
+
+using namespace ska;
+
+struct ska_cache {
+    ska_pool_desc pool;
+    int device = 0;
+    int num_cus = 256;
+    int nt = 0;
+    int8_t tslot[9];
+    int64_t page_stride = 0;
+    std::vector<double> range;  // [hkv][2]
+    double *d_cos2 = nullptr, *d_sin2 = nullptr, *d_cen = nullptr, *d_tau2 = nullptr;
+    float2 *d_lut = nullptr;
+    float *d_rlev = nullptr;
+    uint32_t *d_err = nullptr;
+    void *d_ws = nullptr;
+    size_t ws_bytes = 0;
+    // kernel timing (ska_profile_begin / ska_profile_read)
+    std::vector<hipEvent_t> prof_ev;  // 4 per recorded call
+    int prof_max = 0, prof_n = 0;
+};
+
+namespace {
+
+bool tiers_ok(uint32_t mask) { return mask != 0 && (mask & ~kSupportedTiers) == 0; }
+
+int max_tier(uint32_t mask) {
+    int b = 0;
+    for (int i = 2; i <= 8; ++i)
+        if ((mask >> i) & 1u) b = i;
+    return b;
+}
+
+ska_status check_pool(const ska_pool_desc *p) {
+    if (!p) return SKA_ERR_INVALID;
+    if (p->d != 64 && p->d != 128) return (p->d > 0 && p->d % 4 == 0) ? SKA_ERR_UNSUPPORTED : SKA_ERR_INVALID;
+    if (p->num_kv_heads < 1 || p->page_size != kPage || p->num_pages < 1) return SKA_ERR_INVALID;
+    if (p->radius_mode != SKA_RADIUS_UNIFORM && p->radius_mode != SKA_RADIUS_LOG) return SKA_ERR_INVALID;
+    if (p->radius_bits != 8) return SKA_ERR_UNSUPPORTED;
+    if (!tiers_ok(p->tier_mask)) return SKA_ERR_INVALID;
+    if (p->query_mode != SKA_Q_CODED && p->query_mode != SKA_Q_EXACT) return SKA_ERR_INVALID;
+    if (!p->kcode || !p->rcode || !p->v || !p->page_bits) return SKA_ERR_INVALID;
+    return SKA_OK;
+}
+
+bool same_shape(const ska_pool_desc &a, const ska_pool_desc &b) {
+    return a.d == b.d && a.num_kv_heads == b.num_kv_heads && a.page_size == b.page_size &&
+           a.num_pages == b.num_pages && a.radius_mode == b.radius_mode && a.radius_bits == b.radius_bits &&
+           a.tier_mask == b.tier_mask && a.query_mode == b.query_mode;
+}
+
+// cos^2, sin^2 of the bin edges j*pi/2^b for b = 1..8 at offset 2^b - 2.
+void build_thresholds(std::vector<double> &c2, std::vector<double> &s2) {
+    c2.assign(kThrEntries, 0.0);
+    s2.assign(kThrEntries, 0.0);
+    for (int b = 1; b <= 8; ++b) {
+        const int n = 1 << b;
+        c2[thr_off(b)] = 1.0;
+        s2[thr_off(b)] = 0.0;
+        for (int j = 1; j < n; ++j) {
+            const double th = std::ldexp((double)j * M_PI, -b);
+            const double c = std::cos(th), s = std::sin(th);
+            c2[thr_off(b) + j] = c * c;
+            s2[thr_off(b) + j] = s * s;
+        }
+    }
+}
+
+// binary64 (cos, sin) of bin centres in the decode table layout.
+void build_centres(std::vector<double> &cen) {
+    cen.assign(2 * kLutEntries, 0.0);
+    const int tiers[5] = {2, 3, 4, 6, 8};
+    for (int b : tiers) {
+        const int n = 1 << b;
+        for (int c = 0; c < n; ++c) {
+            const double pp = ((double)c + 0.5) * M_PI / (double)n;
+            const double pa = ((double)c + 0.5) * 2.0 * M_PI / (double)n;
+            cen[2 * (lut_polar(b) + c) + 0] = std::cos(pp);
+            cen[2 * (lut_polar(b) + c) + 1] = std::sin(pp);
+            cen[2 * (lut_azimuth(b) + c) + 0] = std::cos(pa);
+            cen[2 * (lut_azimuth(b) + c) + 1] = std::sin(pa);
+        }
+    }
+    for (int c = 0; c < 256; ++c) {
+        cen[2 * (kLutOnes + c) + 0] = 1.0;
+        cen[2 * (kLutOnes + c) + 1] = 1.0;
+    }
+}
+
+// Radius levels and squared edges of one kv head (8 bits).
+void build_radius(int mode, double rlo, double rhi, float *level, double *tau2) {
+    if (!(rhi > 0.0)) {
+        for (int j = 0; j < 256; ++j) level[j] = 0.f;
+        for (int j = 0; j < 255; ++j) tau2[j] = 0.0;
+        return;
+    }
+    if (mode == SKA_RADIUS_UNIFORM) {
+        for (int j = 0; j < 256; ++j) level[j] = (float)(((double)j * rhi) / 255.0);
+        for (int j = 0; j < 255; ++j) {
+            const double e = (((double)j + 0.5) * rhi) / 255.0;
+            tau2[j] = e * e;
+        }
+    } else {
+        if (!(rlo > 0.0)) rlo = rhi;
+        const double L = std::log(rlo), U = std::log(rhi);
+        for (int j = 0; j < 256; ++j) level[j] = (float)std::exp(L + ((double)j * (U - L)) / 255.0);
+        for (int j = 0; j < 255; ++j) {
+            const double e = std::exp(L + (((double)j + 0.5) * (U - L)) / 255.0);
+            tau2[j] = e * e;
+        }
+    }
+}
+
+template <class T>
+hipError_t upload(T **dst, const T *src, size_t count) {
+    hipError_t e = hipMalloc((void **)dst, count * sizeof(T));
+    if (e != hipSuccess) return e;
+    return hipMemcpy(*dst, src, count * sizeof(T), hipMemcpyHostToDevice);
+}
+
+void prof_clear(ska_cache *c) {
+    for (hipEvent_t e : c->prof_ev) hipEventDestroy(e);
+    c->prof_ev.clear();
+    c->prof_max = c->prof_n = 0;
+}
+
+void release(ska_cache *c) {
+    if (!c) return;
+    prof_clear(c);
+    hipFree(c->d_cos2);
+    hipFree(c->d_sin2);
+    hipFree(c->d_cen);
+    hipFree(c->d_tau2);
+    hipFree(c->d_lut);
+    hipFree(c->d_rlev);
+    hipFree(c->d_err);
+    hipFree(c->d_ws);
+    delete c;
+}
+
+ska_status create(ska_cache **out, const ska_pool_desc *pool) {
+    ska_cache *c = new (std::nothrow) ska_cache();
+    if (!c) return SKA_ERR_NOMEM;
+    c->pool = *pool;
+    if (hipGetDevice(&c->device) != hipSuccess) { delete c; return SKA_ERR_HIP; }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess && cus > 0)
+        c->num_cus = cus;
+    c->nt = 0;
+    for (int b = 0; b <= 8; ++b) c->tslot[b] = 0;
+    for (int b = 2; b <= 8; ++b)
+        if ((pool->tier_mask >> b) & 1u) c->tslot[b] = (int8_t)c->nt++;
+    c->page_stride = (int64_t)pool->num_kv_heads * kPage * record_bytes(pool->d, max_tier(pool->tier_mask));
+
+    std::vector<double> c2, s2, cen;
+    build_thresholds(c2, s2);
+    build_centres(cen);
+    std::vector<float2> lut(kLutEntries);
+    for (int e = 0; e < kLutEntries; ++e) lut[e] = make_float2((float)cen[2 * e], (float)cen[2 * e + 1]);
+    hipError_t e = upload(&c->d_cos2, c2.data(), c2.size());
+    if (e == hipSuccess) e = upload(&c->d_sin2, s2.data(), s2.size());
+    if (e == hipSuccess) e = upload(&c->d_cen, cen.data(), cen.size());
+    if (e == hipSuccess) e = upload(&c->d_lut, lut.data(), lut.size());
+    uint32_t zero = 0;
+    if (e == hipSuccess) e = upload(&c->d_err, &zero, 1);
+    if (e != hipSuccess) {
+        release(c);
+        return e == hipErrorOutOfMemory ? SKA_ERR_NOMEM : SKA_ERR_HIP;
+    }
+    *out = c;
+    return SKA_OK;
+}
+
+ska_status set_range(ska_cache *c, const double *range) {
+    const int hkv = c->pool.num_kv_heads;
+    c->range.assign(range, range + 2 * hkv);
+    std::vector<float> lev(256 * (size_t)hkv);
+    std::vector<double> tau2(255 * (size_t)hkv);
+    for (int g = 0; g < hkv; ++g)
+        build_radius(c->pool.radius_mode, range[2 * g], range[2 * g + 1], lev.data() + 256 * g, tau2.data() + 255 * g);
+    hipFree(c->d_rlev);
+    hipFree(c->d_tau2);
+    c->d_rlev = nullptr;
+    c->d_tau2 = nullptr;
+    hipError_t e = upload(&c->d_rlev, lev.data(), lev.size());
+    if (e == hipSuccess) e = upload(&c->d_tau2, tau2.data(), tau2.size());
+    return e == hipSuccess ? SKA_OK : (e == hipErrorOutOfMemory ? SKA_ERR_NOMEM : SKA_ERR_HIP);
+}
+
+ska_status calibrate(ska_cache *c, const float *keys, int64_t n, hipStream_t s) {
+    const int hkv = c->pool.num_kv_heads;
+    std::vector<unsigned long long> mm(2 * (size_t)hkv);
+    for (int g = 0; g < hkv; ++g) {
+        mm[2 * g + 0] = 0ull;                      // max: +0.0
+        mm[2 * g + 1] = 0x7FF0000000000000ull;     // min positive: +inf
+    }
+    unsigned long long *d_mm = nullptr;
+    if (hipMalloc((void **)&d_mm, mm.size() * sizeof(mm[0])) != hipSuccess) return SKA_ERR_NOMEM;
+    hipError_t e = hipMemcpyAsync(d_mm, mm.data(), mm.size() * sizeof(mm[0]), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = launch_calibrate(keys, n, hkv, c->pool.d, d_mm, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(mm.data(), d_mm, mm.size() * sizeof(mm[0]), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    hipFree(d_mm);
+    if (e != hipSuccess) return SKA_ERR_HIP;
+    std::vector<double> range(2 * (size_t)hkv);
+    for (int g = 0; g < hkv; ++g) {
+        double smax, smin;
+        std::memcpy(&smax, &mm[2 * g + 0], 8);
+        std::memcpy(&smin, &mm[2 * g + 1], 8);
+        const double rhi = std::sqrt(smax);
+        range[2 * g + 0] = std::isinf(smin) ? rhi : std::sqrt(smin);
+        range[2 * g + 1] = rhi;
+    }
+    return set_range(c, range.data());
+}
+
+ska_status ensure_ws(ska_cache *c, size_t bytes) {
+    if (bytes <= c->ws_bytes) return SKA_OK;
+    if (c->d_ws) {
+        if (hipFree(c->d_ws) != hipSuccess) return SKA_ERR_HIP;  // hipFree waits for work using it
+        c->d_ws = nullptr;
+        c->ws_bytes = 0;
+    }
+    size_t want = bytes + bytes / 4;
+    if (hipMalloc(&c->d_ws, want) != hipSuccess) {
+        c->d_ws = nullptr;
+        return SKA_ERR_NOMEM;
+    }
+    c->ws_bytes = want;
+    return SKA_OK;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ska_status_string(ska_status s) {
+    switch (s) {
+        case SKA_OK: return "ok";
+        case SKA_ERR_INVALID: return "invalid argument";
+        case SKA_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case SKA_ERR_HIP: return "HIP runtime error";
+        case SKA_ERR_NOMEM: return "out of memory";
+    }
+    return "unknown status";
+}
+
+ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool, const float *keys,
+                           const uint16_t *values, const int64_t *slot, int64_t n,
+                           const double *radius_range, void *stream) {
+    if (!cache) return SKA_ERR_INVALID;
+    ska_status st = check_pool(pool);
+    if (st != SKA_OK) return st;
+    if (n < 0 || (n > 0 && (!keys || !slot))) return SKA_ERR_INVALID;
+    if (*cache && !same_shape((*cache)->pool, *pool)) return SKA_ERR_INVALID;
+    if (!*cache && !radius_range && n == 0) return SKA_ERR_INVALID;  // nothing to calibrate on
+    if (radius_range && !*cache) {
+        for (int g = 0; g < pool->num_kv_heads; ++g) {
+            const double lo = radius_range[2 * g], hi = radius_range[2 * g + 1];
+            if (!std::isfinite(lo) || !std::isfinite(hi) || lo < 0.0 || hi < 0.0 || lo > hi) return SKA_ERR_INVALID;
+        }
+    }
+    hipStream_t s = (hipStream_t)stream;
+    ska_cache *c = *cache;
+    bool created = false;
+    if (!c) {
+        st = create(&c, pool);
+        if (st != SKA_OK) return st;
+        created = true;
+        st = radius_range ? set_range(c, radius_range) : calibrate(c, keys, n, s);
+        if (st != SKA_OK) {
+            release(c);
+            return st;
+        }
+    }
+    c->pool = *pool;  // same shape; pointers may move
+    if (n > 0) {
+        EncodeArgs a{};
+        a.keys = keys;
+        a.values = values;
+        a.slot = slot;
+        a.n = n;
+        a.d = pool->d;
+        a.hkv = pool->num_kv_heads;
+        a.num_pages = pool->num_pages;
+        a.tier_mask = pool->tier_mask;
+        a.page_bits = pool->page_bits;
+        a.page_off = pool->page_off;
+        a.page_stride = c->page_stride;
+        a.kcode = pool->kcode;
+        a.rcode = pool->rcode;
+        a.v = pool->v;
+        a.tau2 = c->d_tau2;
+        a.tab = CodeTables{c->d_cos2, c->d_sin2, c->d_cen};
+        a.err = c->d_err;
+        if (launch_encode(a, s) != hipSuccess) {
+            if (created) release(c);
+            return SKA_ERR_HIP;
+        }
+    }
+    *cache = c;
+    return SKA_OK;
+}
+
+ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num_q_heads,
+                                const int32_t *block_table, int max_pages, const int32_t *seq_lens,
+                                float scale, int num_splits, float *out, float *logits_dbg, void *stream) {
+    if (!c) return SKA_ERR_INVALID;
+    if (batch < 0 || num_q_heads < 1 || max_pages < 1 || num_splits < 0) return SKA_ERR_INVALID;
+    if (!std::isfinite(scale) || scale < 0.f) return SKA_ERR_INVALID;
+    const int hkv = c->pool.num_kv_heads, d = c->pool.d;
+    if (num_q_heads % hkv != 0) return SKA_ERR_INVALID;
+    const int G = num_q_heads / hkv;
+    if (G != 1 && G != 2 && G != 4) return SKA_ERR_UNSUPPORTED;
+    if (batch == 0) return SKA_OK;
+    if (!q || !block_table || !seq_lens || !out) return SKA_ERR_INVALID;
+    if ((int64_t)batch * num_q_heads > (1ll << 30)) return SKA_ERR_UNSUPPORTED;
+    if (scale == 0.f) scale = 1.0f / std::sqrt((float)d);
+
+    // split policy: pages per split (a multiple of the 4 waves)
+    int pps;
+    if (num_splits > 0) {
+        pps = (max_pages + num_splits - 1) / num_splits;
+    } else {
+        const int64_t total = (int64_t)batch * hkv * max_pages;
+        const int64_t target = 4ll * c->num_cus;  // workgroups
+        pps = (int)((total + target - 1) / target);
+    }
+    pps = ((pps + kWaves - 1) / kWaves) * kWaves;
+    if (pps < kWaves) pps = kWaves;
+    const int nsplit = (max_pages + pps - 1) / pps;
+    if ((int64_t)nsplit * hkv > (1ll << 31) || batch > 65535 || nsplit > (1 << 30)) return SKA_ERR_UNSUPPORTED;
+
+    const size_t uq_n = (size_t)batch * hkv * c->nt * d * G;
+    const size_t po_n = (size_t)batch * num_q_heads * nsplit * d;
+    const size_t pm_n = (size_t)batch * num_q_heads * nsplit * 2;
+    const size_t off_po = align256(uq_n * 4), off_pm = off_po + align256(po_n * 4);
+    ska_status st = ensure_ws(c, off_pm + align256(pm_n * 4));
+    if (st != SKA_OK) return st;
+    char *ws = (char *)c->d_ws;
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t *ev = nullptr;
+    if (c->prof_n < c->prof_max) ev = &c->prof_ev[4 * (size_t)c->prof_n++];
+    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return SKA_ERR_HIP;
+
+    QPrepArgs qa{};
+    qa.q = q;
+    qa.B = batch;
+    qa.hq = num_q_heads;
+    qa.hkv = hkv;
+    qa.d = d;
+    qa.G = G;
+    qa.tier_mask = c->pool.tier_mask;
+    qa.nt = c->nt;
+    qa.query_mode = c->pool.query_mode;
+    qa.scale = scale;
+    qa.tab = CodeTables{c->d_cos2, c->d_sin2, c->d_cen};
+    qa.uq = (float *)ws;
+    if (launch_qprep(qa, s) != hipSuccess) return SKA_ERR_HIP;
+    if (ev && hipEventRecord(ev[1], s) != hipSuccess) return SKA_ERR_HIP;
+
+    DecodeArgs da{};
+    da.kcode = c->pool.kcode;
+    da.page_off = c->pool.page_off;
+    da.rcode = c->pool.rcode;
+    da.v = c->pool.v;
+    da.page_bits = c->pool.page_bits;
+    da.block_table = block_table;
+    da.seq_lens = seq_lens;
+    da.uq = (const float *)ws;
+    da.lut = c->d_lut;
+    da.rlev = c->d_rlev;
+    da.part_o = (float *)(ws + off_po);
+    da.part_ml = (float *)(ws + off_pm);
+    da.logits = logits_dbg;
+    da.err = c->d_err;
+    da.num_pages = c->pool.num_pages;
+    da.page_stride = c->page_stride;
+    da.hkv = hkv;
+    da.hq = num_q_heads;
+    da.max_pages = max_pages;
+    da.pps = pps;
+    da.nsplit = nsplit;
+    da.tier_mask = c->pool.tier_mask;
+    da.nt = c->nt;
+    for (int b = 0; b <= 8; ++b) da.tslot[b] = c->tslot[b];
+    if (launch_decode(da, d, G, batch, s) != hipSuccess) return SKA_ERR_HIP;
+    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return SKA_ERR_HIP;
+
+    MergeArgs ma{};
+    ma.part_o = da.part_o;
+    ma.part_ml = da.part_ml;
+    ma.seq_lens = seq_lens;
+    ma.out = out;
+    ma.hq = num_q_heads;
+    ma.d = d;
+    ma.max_pages = max_pages;
+    ma.pps = pps;
+    ma.nsplit = nsplit;
+    if (launch_merge(ma, batch, s) != hipSuccess) return SKA_ERR_HIP;
+    if (ev && hipEventRecord(ev[3], s) != hipSuccess) return SKA_ERR_HIP;
+    return SKA_OK;
+}
+
+ska_status ska_profile_begin(ska_cache *c, int max_calls) {
+    if (!c || max_calls < 0 || max_calls > (1 << 20)) return SKA_ERR_INVALID;
+    prof_clear(c);
+    c->prof_ev.assign(4 * (size_t)max_calls, nullptr);
+    for (auto &e : c->prof_ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            prof_clear(c);
+            return SKA_ERR_HIP;
+        }
+    }
+    c->prof_max = max_calls;
+    c->prof_n = 0;
+    return SKA_OK;
+}
+
+ska_status ska_profile_read(ska_cache *c, float *ms_out, int max_calls, int *n_out) {
+    if (!c || !n_out || max_calls < 0 || (max_calls > 0 && !ms_out)) return SKA_ERR_INVALID;
+    const int n = c->prof_n < max_calls ? c->prof_n : max_calls;
+    for (int i = 0; i < n; ++i) {
+        hipEvent_t *ev = &c->prof_ev[4 * (size_t)i];
+        if (hipEventSynchronize(ev[3]) != hipSuccess) return SKA_ERR_HIP;
+        for (int k = 0; k < 3; ++k)
+            if (hipEventElapsedTime(&ms_out[3 * i + k], ev[k], ev[k + 1]) != hipSuccess) return SKA_ERR_HIP;
+    }
+    *n_out = n;
+    return SKA_OK;
+}
+
+ska_status ska_get_radius_range(const ska_cache *c, double *range_out) {
+    if (!c || !range_out) return SKA_ERR_INVALID;
+    std::memcpy(range_out, c->range.data(), c->range.size() * sizeof(double));
+    return SKA_OK;
+}
+
+ska_status ska_device_errors(ska_cache *c, void *stream, uint32_t *flags_out) {
+    if (!c || !flags_out) return SKA_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t v = 0, zero = 0;
+    hipError_t e = hipMemcpyAsync(&v, c->d_err, 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->d_err, &zero, 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return SKA_ERR_HIP;
+    *flags_out = v;
+    return SKA_OK;
+}
+
+void ska_free(ska_cache *c) { release(c); }
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// ska_internal.h -- shared between the host library (ska_api.cpp) and the
+// HIP kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ska {
+
+constexpr int kPage = 16;
+constexpr int kWaves = 4;               // waves per decode workgroup
+constexpr int kThreads = 64 * kWaves;
+
+// Bytes of one key record: 16 * ceil((d-1) * b / 128).
+__host__ __device__ constexpr int record_bytes(int d, int b) { return 16 * (((d - 1) * b + 127) / 128); }
+
+// Layout of the decode lookup table (float2 entries, staged into LDS).  Per
+// tier: 2^b polar (cos, sin) of bin centres (c + 1/2) pi / 2^b, then 2^b
+// azimuth (cos, sin) of (c + 1/2) 2 pi / 2^b.  A final block of 256 (1, 1)
+// entries serves the padding slot after the azimuth of the last slice.
+__host__ __device__ constexpr int lut_polar(int b) {
+    return b == 2 ? 0 : b == 3 ? 8 : b == 4 ? 24 : b == 6 ? 56 : 184;
+}
+__host__ __device__ constexpr int lut_azimuth(int b) { return lut_polar(b) + (1 << b); }
+constexpr int kLutOnes = 696;
+constexpr int kLutEntries = 952;
+
+// Encode-side angle threshold tables (binary64): for every b in 1..8, 2^b
+// entries of cos^2 and sin^2 of the bin edges j*pi/2^b, at offset
+// thr_off(b) = 2^b - 2.
+__host__ __device__ constexpr int thr_off(int b) { return (1 << b) - 2; }
+constexpr int kThrEntries = 510;
+
+constexpr uint32_t kSupportedTiers = (1u << 2) | (1u << 3) | (1u << 4) | (1u << 6) | (1u << 8);
+
+struct CodeTables {
+    const double *cos2;     // [kThrEntries]
+    const double *sin2;     // [kThrEntries]
+    const double *cen_cs;   // [kLutEntries][2] binary64 cos, sin of bin centres (same layout as the LUT)
+};
+
+struct EncodeArgs {
+    const float *keys;
+    const uint16_t *values;
+    const int64_t *slot;
+    int64_t n;
+    int d, hkv;
+    int64_t num_pages;
+    uint32_t tier_mask;
+    const uint8_t *page_bits;
+    const uint64_t *page_off;
+    int64_t page_stride;     // bytes per physical page when page_off == NULL
+    uint8_t *kcode;
+    uint8_t *rcode;
+    uint16_t *v;
+    const double *tau2;      // [hkv][255] squared radius edges
+    CodeTables tab;
+    uint32_t *err;
+};
+
+struct QPrepArgs {
+    const float *q;          // [B][hq][d]
+    int B, hq, hkv, d, G;
+    uint32_t tier_mask;
+    int nt;                  // tiers present in the mask
+    int query_mode;
+    float scale;             // softmax scale
+    CodeTables tab;
+    float *uq;               // [B][hkv][nt][4][d/4][G]
+};
+
+struct DecodeArgs {
+    const uint8_t *kcode;
+    const uint64_t *page_off;
+    const uint8_t *rcode;
+    const uint16_t *v;
+    const uint8_t *page_bits;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    const float *uq;
+    const float2 *lut;       // [kLutEntries]
+    const float *rlev;       // [hkv][256] radius levels
+    float *part_o;           // [B][hq][nsplit][d]
+    float *part_ml;          // [B][hq][nsplit][2]
+    float *logits;           // debug [B][hq][max_pages*16] or NULL
+    uint32_t *err;
+    int64_t num_pages;
+    int64_t page_stride;
+    int hkv, hq, max_pages;
+    int pps;                 // pages per split (multiple of kWaves)
+    int nsplit;
+    uint32_t tier_mask;
+    int nt;
+    int8_t tslot[9];         // tier b -> index among the tiers present
+};
+
+struct MergeArgs {
+    const float *part_o;
+    const float *part_ml;
+    const int32_t *seq_lens;
+    float *out;
+    int hq, d, max_pages, pps, nsplit;
+};
+
+hipError_t launch_calibrate(const float *keys, int64_t n, int hkv, int d, unsigned long long *minmax,
+                            hipStream_t s);
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
+hipError_t launch_qprep(const QPrepArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, int B, hipStream_t s);
+
+}  // namespace ska

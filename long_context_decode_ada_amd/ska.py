@@ -1,0 +1,212 @@
+"""ctypes binding of the C ABI in include/ska.h (libska.so).
+
+Argument marshalling only: every step of encode and decode runs in the HIP
+kernels of libska.so.  PyTorch supplies device memory and the stream.  There
+is no fallback: if libska.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libska.so")
+
+SKA_OK, SKA_ERR_INVALID, SKA_ERR_UNSUPPORTED, SKA_ERR_HIP, SKA_ERR_NOMEM = range(5)
+RADIUS_UNIFORM, RADIUS_LOG = 0, 1
+Q_CODED, Q_EXACT = 0, 1
+PAGE = 16
+DEVERR_SLOT, DEVERR_PAGE, DEVERR_TIER = 1, 2, 4
+
+SYMBOLS = ("ska_encode_keys", "ska_decode_attention", "ska_get_radius_range", "ska_device_errors",
+           "ska_profile_begin", "ska_profile_read", "ska_free", "ska_status_string")
+
+
+class SkaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int),
+        ("num_kv_heads", ctypes.c_int),
+        ("page_size", ctypes.c_int),
+        ("num_pages", ctypes.c_int64),
+        ("radius_mode", ctypes.c_int),
+        ("radius_bits", ctypes.c_int),
+        ("tier_mask", ctypes.c_uint32),
+        ("query_mode", ctypes.c_int),
+        ("kcode", ctypes.c_void_p),
+        ("page_off", ctypes.c_void_p),
+        ("rcode", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("page_bits", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libska.so is not built (python -m long_context_decode_ada_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i, i64, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        L.ska_encode_keys.restype = i
+        L.ska_encode_keys.argtypes = [ctypes.POINTER(P), ctypes.POINTER(PoolDesc), P, P, P, i64, P, P]
+        L.ska_decode_attention.restype = i
+        L.ska_decode_attention.argtypes = [P, P, i, i, P, i, P, f, i, P, P, P]
+        L.ska_get_radius_range.restype = i
+        L.ska_get_radius_range.argtypes = [P, P]
+        L.ska_device_errors.restype = i
+        L.ska_device_errors.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
+        L.ska_profile_begin.restype = i
+        L.ska_profile_begin.argtypes = [P, i]
+        L.ska_profile_read.restype = i
+        L.ska_profile_read.argtypes = [P, P, i, ctypes.POINTER(ctypes.c_int)]
+        L.ska_free.restype = None
+        L.ska_free.argtypes = [P]
+        L.ska_status_string.restype = ctypes.c_char_p
+        L.ska_status_string.argtypes = [i]
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().ska_status_string(int(s)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(s: int, what: str):
+    if s != SKA_OK:
+        raise SkaError(s, what)
+
+
+class DevicePools:
+    """Caller-owned device pools in the library's layout (torch tensors)."""
+
+    def __init__(self, *, d: int, hkv: int, num_pages: int, tier_mask: int, radius_mode: int,
+                 page_bits: torch.Tensor, kcode_bytes: int, page_off: Optional[torch.Tensor] = None,
+                 query_mode: int = Q_CODED, device="cuda", poison: bool = True):
+        self.d, self.hkv, self.num_pages = d, hkv, num_pages
+        self.tier_mask, self.radius_mode, self.query_mode = tier_mask, radius_mode, query_mode
+        self.page_bits = page_bits.to(device=device, dtype=torch.uint8).contiguous()
+        self.page_off = None if page_off is None else page_off.to(device=device, dtype=torch.int64).contiguous()
+        fill = 0xFF if poison else 0
+        self.kcode = torch.full((kcode_bytes,), fill, dtype=torch.uint8, device=device)
+        self.rcode = torch.full((num_pages * hkv * PAGE,), fill, dtype=torch.uint8, device=device)
+        # bf16 NaN poison (0x7FC0) or zero, stored as raw 16-bit patterns
+        self.v = torch.full((num_pages * hkv * d * PAGE,), 0x7FC0 if poison else 0, dtype=torch.int16, device=device)
+
+    @classmethod
+    def for_workload(cls, w, device="cuda", poison=True, query_mode=Q_CODED):
+        off = None if w.page_off is None else torch.from_numpy(w.page_off.view(np.int64))
+        return cls(d=w.d, hkv=w.hkv, num_pages=w.num_pages, tier_mask=w.tier_mask, radius_mode=w.radius_mode,
+                   page_bits=torch.from_numpy(w.page_bits), kcode_bytes=w.kcode_bytes, page_off=off,
+                   query_mode=query_mode, device=device, poison=poison)
+
+    def desc(self) -> PoolDesc:
+        return PoolDesc(self.d, self.hkv, PAGE, self.num_pages, self.radius_mode, 8, self.tier_mask,
+                        self.query_mode, self.kcode.data_ptr(),
+                        None if self.page_off is None else self.page_off.data_ptr(),
+                        self.rcode.data_ptr(), self.v.data_ptr(), self.page_bits.data_ptr())
+
+    def to_host(self) -> dict:
+        return {"kcode": self.kcode.cpu().numpy(), "rcode": self.rcode.cpu().numpy(),
+                "v": self.v.cpu().numpy().view(np.uint16)}
+
+
+class Cache:
+    """Owns one ska_cache handle (freed with ska_free)."""
+
+    def __init__(self, pools: DevicePools):
+        self.pools = pools
+        self.handle = ctypes.c_void_p(None)
+
+    def free(self):
+        if self.handle.value:
+            lib().ska_free(self.handle)
+            self.handle = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def encode_keys(cache: Cache, keys: torch.Tensor, values: Optional[torch.Tensor], slot: torch.Tensor,
+                radius_range: Optional[np.ndarray] = None, stream=None) -> Cache:
+    """ska_encode_keys: keys fp32 [n][hkv][d], values bf16 bits (int16/uint16/bf16) [n][hkv][d] or
+    None, slot int64 [n], radius_range host [hkv][2] or None."""
+    n = int(keys.shape[0]) if keys is not None else 0
+    desc = cache.pools.desc()
+    rr = None
+    if radius_range is not None:
+        rr = np.ascontiguousarray(radius_range, np.float64)
+    s = lib().ska_encode_keys(ctypes.byref(cache.handle), ctypes.byref(desc), _ptr(keys), _ptr(values),
+                              _ptr(slot), n, None if rr is None else rr.ctypes.data_as(ctypes.c_void_p),
+                              _stream(stream))
+    _check(s, "ska_encode_keys")
+    return cache
+
+
+def decode_attention(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                     scale: float = 0.0, num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                     logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ska_decode_attention: q fp32 [B][hq][d], block_table int32 [B][max_pages], seq_lens int32 [B];
+    returns out fp32 [B][hq][d].  logits (fp32 [B][hq][max_pages*16]) is filled if given."""
+    B, hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    s = lib().ska_decode_attention(cache.handle, _ptr(q), B, hq, _ptr(block_table), int(block_table.shape[1]),
+                                   _ptr(seq_lens), float(scale), int(num_splits), _ptr(out), _ptr(logits),
+                                   _stream(stream))
+    _check(s, "ska_decode_attention")
+    return out
+
+
+def radius_range(cache: Cache) -> np.ndarray:
+    r = np.zeros((cache.pools.hkv, 2), np.float64)
+    _check(lib().ska_get_radius_range(cache.handle, r.ctypes.data_as(ctypes.c_void_p)), "ska_get_radius_range")
+    return r
+
+
+def device_errors(cache: Cache, stream=None) -> int:
+    v = ctypes.c_uint32(0)
+    _check(lib().ska_device_errors(cache.handle, _stream(stream), ctypes.byref(v)), "ska_device_errors")
+    return int(v.value)
+
+
+def profile_begin(cache: Cache, max_calls: int):
+    _check(lib().ska_profile_begin(cache.handle, int(max_calls)), "ska_profile_begin")
+
+
+def profile_read(cache: Cache, max_calls: int) -> np.ndarray:
+    """[calls][3] kernel milliseconds (query prep, decode, merge)."""
+    ms = np.zeros((max(1, max_calls), 3), np.float32)
+    n = ctypes.c_int(0)
+    _check(lib().ska_profile_read(cache.handle, ms.ctypes.data_as(ctypes.c_void_p), int(max_calls),
+                                  ctypes.byref(n)), "ska_profile_read")
+    return ms[: n.value]
+
+
+def free(cache: Cache):
+    cache.free()

@@ -1,0 +1,121 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds.
+
+Bars: encoded pools (angle-code records, radius codes, scattered values)
+bit-exact, including bytes that must stay untouched; radius range bit-exact;
+logits within 1e-3 of their bound scale*|q|*r~; outputs within 2e-3."""
+import numpy as np
+import pytest
+
+from long_context_decode_ada_amd import workloads as W
+from oracle import oracle as O
+from tests.parity_util import compare, gpu_run, oracle_run, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    ("tiny", 1.0, None),
+    ("gqa_t32k", 1 / 32, None),       # T = 1024, B = 8, 32/8 heads, b = 4
+    ("long_t128k", 1 / 128, None),    # T = 1024, B = 1, b = 3
+    ("ragged_b64", 1 / 32, None),     # lengths 16..2048
+    ("mixed_tiers", 1 / 16, 4),       # 65 resident pages of mixed tiers per sequence
+]
+
+
+@pytest.fixture(scope="module")
+def runs():
+    cache = {}
+
+    def get(name, scale, batch):
+        key = (name, scale, batch)
+        if key not in cache:
+            say("[gpu parity] workload", key)
+            w = W.make(name, scale, batch=batch)
+            g = gpu_run(w)
+            rng = O.calibrate(w.keys)
+            o = oracle_run(w, rng)
+            cache[key] = (w, g, o, rng)
+        return cache[key]
+    return get
+
+
+@pytest.mark.parametrize("name,scale,batch", SMALL)
+def test_encode_is_bit_exact(runs, name, scale, batch):
+    w, g, o, rng = runs(name, scale, batch)
+    assert np.array_equal(g["range"], rng), (g["range"], rng)
+    for k in ("kcode", "rcode", "v"):
+        a, b = g["pools"][k], o["pools"][k]
+        nd = int(np.count_nonzero(a != b))
+        say("[%s] %s mismatching bytes: %d of %d" % (name, k, nd, a.size))
+        assert nd == 0
+    assert g["errors"] == 0
+
+
+@pytest.mark.parametrize("name,scale,batch", SMALL)
+def test_decode_matches_oracle(runs, name, scale, batch):
+    w, g, o, rng = runs(name, scale, batch)
+    compare(w, g, o, rng, label=name)
+
+
+def test_split_count_and_determinism():
+    w = W.make("gqa_t32k", 1 / 32, batch=3)
+    rng = O.calibrate(w.keys)
+    o = oracle_run(w, rng)
+    base = None
+    for ns in (1, 3, 16, 64):
+        g = gpu_run(w, num_splits=ns, repeat=2)
+        assert np.array_equal(g["outs"][0], g["outs"][1]), "run-to-run difference at %d splits" % ns
+        compare(w, g, o, rng, label="splits=%d" % ns)
+        if base is None:
+            base = g
+        else:
+            assert np.array_equal(g["logits"], base["logits"], equal_nan=True)
+            assert np.abs(g["out"] - base["out"]).max() < 1e-5
+
+
+def test_ragged_edges_zero_one_and_page_boundaries():
+    w = W.make("gqa_t32k", 1 / 32, batch=8)          # 1024 tokens encoded per sequence
+    lens = np.array([0, 1, 15, 16, 17, 31, 33, 1024], np.int32)
+    rng = O.calibrate(w.keys)
+    g = gpu_run(w, seq_lens=lens)
+    o = oracle_run(w, rng, seq_lens=lens)
+    assert not g["out"][0].any()
+    compare(w, g, o, rng, seq_lens=lens, label="edge lengths")
+
+
+@pytest.mark.parametrize("hq", [8, 16])
+def test_group_sizes_one_and_two(hq):
+    w = W.make("gqa_t32k", 1 / 64, batch=2)
+    q = np.ascontiguousarray(w.q[:, :hq])
+    rng = O.calibrate(w.keys)
+    g = gpu_run(w, q=q)
+    o = oracle_run(w, rng, q=q)
+    compare(w, g, o, rng, q=q, label="G=%d" % (hq // 8))
+
+
+def test_query_exact_variant():
+    w = W.make("mixed_tiers", 1 / 32, batch=2)
+    rng = O.calibrate(w.keys)
+    g = gpu_run(w, query_mode=1)
+    o = oracle_run(w, rng, query_mode=1)
+    compare(w, g, o, rng, label="exact query")
+
+
+def test_given_radius_range_and_uniform_d128():
+    w = W.make("gqa_t32k", 1 / 64, batch=2)
+    w.radius_mode = W.UNIFORM
+    rng = np.tile([0.0, 25.0], (w.hkv, 1))           # some keys exceed R_hi: code 255
+    g = gpu_run(w, radius_range=rng)
+    assert np.array_equal(g["range"], rng)
+    o = oracle_run(w, rng)
+    for k in ("kcode", "rcode", "v"):
+        assert np.array_equal(g["pools"][k], o["pools"][k]), k
+    compare(w, g, o, rng, label="uniform radius, given range")
+
+
+def test_no_poison_read_from_unused_pages():
+    """With NaN/0xFF poison everywhere outside the written slots (shared pool
+    with unused pages and partial last pages), outputs are finite."""
+    w = W.make("ragged_b64", 1 / 64, batch=16)
+    g = gpu_run(w, poison=True)
+    assert np.isfinite(g["out"]).all()
