@@ -168,72 +168,84 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Query preparation: one workgroup of d threads per (sequence, query head).
-// Thread a owns angle a: its suffix sum (same backward order as the keys),
-// its code at every tier present, and then component a of the decoded
-// direction u(centres(c_q)) (binary64), stored premultiplied by
-// scale * |q| * log2(e) as fp32 in the decode kernel's register layout
+// The query's suffix sums are formed by one thread in the same backward order
+// as the keys'; thread a then finds the code of angle a at every tier present
+// (bisection over LDS copies of the edge tables), and the decoded direction
+// u_a = (prod_{k<a} sin c_k) * cos c_a follows from a parallel product scan of
+// the bin-centre sines (binary64).  Output, per tier, the unit vector as fp16
+// in the decode kernel's register layout
 //   uq[((((seq*hkv + kvh)*nt + tier)*4 + slice)*(d/4) + i)*G + h_in_group],
-// component a = slice*(d/4) + i.
+// component a = slice*(d/4) + i, and sq = scale * |q| * log2(e) in fp32.
 __global__ __launch_bounds__(128) void k_qprep(QPrepArgs A) {
     __shared__ float xs[128];
-    __shared__ uint8_t cq[5][128];
-    __shared__ double tot;
+    __shared__ double Ts[129];
+    __shared__ double thr[4][256];
+    __shared__ double cen[4][256];   // polar cos, polar sin, azimuth cos, azimuth sin
+    __shared__ double scan[128];
     const int d = A.d;
     const int a = threadIdx.x;
     const int seq = blockIdx.x / A.hq, h = blockIdx.x % A.hq;
-    const float *qv = A.q + ((int64_t)seq * A.hq + h) * d;
-    xs[a] = qv[a];
+    xs[a] = A.q[((int64_t)seq * A.hq + h) * d + a];
     __syncthreads();
     if (a == 0) {
         double T = (double)xs[d - 1] * (double)xs[d - 1];
-        for (int k = d - 2; k >= 0; --k) T = T + (double)xs[k] * (double)xs[k];
-        tot = T;
+        Ts[d - 1] = T;
+        for (int k = d - 2; k >= 0; --k) {
+            T = T + (double)xs[k] * (double)xs[k];
+            Ts[k] = T;
+        }
     }
+    __syncthreads();
+    const double qn = sqrt(Ts[0]);
+    if (a == 0) A.sq[(int64_t)seq * A.hq + h] = (float)((double)A.scale * qn * 1.4426950408889634);
+    const int G = A.G, kvh = h / G, hg = h % G;
+    const int slice = a / (d / 4), i = a % (d / 4);
     int ti = 0;
     for (int b = 2; b <= 8; ++b) {
         if (!((A.tier_mask >> b) & 1u)) continue;
-        if (a <= d - 2) {
-            int c;
-            if (a == d - 2) {
-                c = azimuth_code((double)xs[d - 2], (double)xs[d - 1], b, A.tab.cos2 + thr_off(b - 1),
-                                 A.tab.sin2 + thr_off(b - 1));
-            } else {
-                double T = (double)xs[d - 1] * (double)xs[d - 1];
-                for (int k = d - 2; k > a; --k) T = T + (double)xs[k] * (double)xs[k];
-                c = polar_code((double)xs[a], T, b, A.tab.cos2 + thr_off(b), A.tab.sin2 + thr_off(b));
-            }
-            cq[ti][a] = (uint8_t)c;
+        const int n = 1 << b;
+        for (int e = a; e < n; e += d) {
+            thr[0][e] = A.tab.cos2[thr_off(b) + e];
+            thr[1][e] = A.tab.sin2[thr_off(b) + e];
+            cen[0][e] = A.tab.cen_cs[2 * (lut_polar(b) + e) + 0];
+            cen[1][e] = A.tab.cen_cs[2 * (lut_polar(b) + e) + 1];
+            cen[2][e] = A.tab.cen_cs[2 * (lut_azimuth(b) + e) + 0];
+            cen[3][e] = A.tab.cen_cs[2 * (lut_azimuth(b) + e) + 1];
         }
-        ++ti;
-    }
-    __syncthreads();
-    const double qn = sqrt(tot);
-    const double mul = (double)A.scale * qn * 1.4426950408889634;  // log2(e)
-    const int G = A.G, kvh = h / G, hg = h % G;
-    const int slice = a / (d / 4), i = a % (d / 4);
-    ti = 0;
-    for (int b = 2; b <= 8; ++b) {
-        if (!((A.tier_mask >> b) & 1u)) continue;
+        for (int e = a; e < n / 2; e += d) {
+            thr[2][e] = A.tab.cos2[thr_off(b - 1) + e];
+            thr[3][e] = A.tab.sin2[thr_off(b - 1) + e];
+        }
+        __syncthreads();
         double u;
         if (A.query_mode == 1) {
             u = qn > 0.0 ? (double)xs[a] / qn : 0.0;
         } else {
-            // u_a = (prod_{k<a} sin phi_k) * cos phi_a ; u_{d-1} = prod_{k<d-1} sin phi_k
-            double P = 1.0;
-            const int kmax = a < d - 1 ? a : d - 1;
-            for (int k = 0; k < kmax; ++k) {
-                const int e = (k == d - 2 ? lut_azimuth(b) : lut_polar(b)) + cq[ti][k];
-                P = P * A.tab.cen_cs[2 * e + 1];
+            double cs = 1.0, sn = 1.0;
+            if (a < d - 2) {
+                const int c = polar_code((double)xs[a], Ts[a + 1], b, thr[0], thr[1]);
+                cs = cen[0][c];
+                sn = cen[1][c];
+            } else if (a == d - 2) {
+                const int c = azimuth_code((double)xs[d - 2], (double)xs[d - 1], b, thr[2], thr[3]);
+                cs = cen[2][c];
+                sn = cen[3][c];
             }
-            if (a < d - 1) {
-                const int e = (a == d - 2 ? lut_azimuth(b) : lut_polar(b)) + cq[ti][a];
-                u = P * A.tab.cen_cs[2 * e + 0];
-            } else {
-                u = P;
+            // inclusive product scan of the sines over the components
+            scan[a] = sn;
+            __syncthreads();
+            for (int off = 1; off < d; off <<= 1) {
+                const double v = (a >= off) ? scan[a - off] : 1.0;
+                __syncthreads();
+                scan[a] *= v;
+                __syncthreads();
             }
+            const double P = (a == 0) ? 1.0 : scan[a - 1];
+            u = P * cs;   // the last component has cs = 1: u = prod of all d-1 sines
         }
         const int64_t idx = (((((int64_t)seq * A.hkv + kvh) * A.nt + ti) * 4 + slice) * (d / 4) + i) * G + hg;
-        A.uq[idx] = (float)(u * mul);
+        A.uq[idx] = (_Float16)(float)u;
+        __syncthreads();   // the tables are refilled for the next tier
         ++ti;
     }
 }

@@ -21,8 +21,12 @@
 //    the b-bit code.  The four slices are joined by a 4-lane exclusive
 //    product scan of the slice sine products (DPP quad permutes):
 //    f_h = sum_j C_j F_h,j with C_j = prod_{i<j} S_i.
-//  * The query side uq = scale * |q| * log2(e) * u(centres(c_q)) is prepared
-//    once per step (k_qprep) and held in registers; logits are in log2 units.
+//  * The query side, the unit vector uq = u(centres(c_q)) per tier, is
+//    prepared once per step (k_qprep) as fp16 pairs and held packed in
+//    registers; v_fma_mix_f32 multiplies a half by the fp32 w and accumulates
+//    in fp32.  Rounding uq to fp16 moves f by at most 2^-11 (Cauchy-Schwarz
+//    over two unit vectors).  The logit is sq_h * r~ * f with
+//    sq_h = scale * |q_h| * log2(e) in fp32, so logits are in log2 units.
 //  * Softmax: online, per head, with the running max raised only when a logit
 //    exceeds it by more than 8 (a wave ballot); probabilities are bounded by
 //    2^8, which fp32 accumulation absorbs.
@@ -33,7 +37,13 @@
 //    keeps 16 mantissa bits of P; V enters as stored (bf16), dimension-major
 //    pages giving each lane its 4 consecutive tokens as one 8-byte load.
 //  * Split-T: each workgroup merges its 4 waves in LDS and writes one
-//    (m, l, o[d]) partial per query head; k_merge combines the splits.
+//    (m, l, o[d]) partial per query head; a second kernel (k_merge) combines
+//    the splits.  (Combining them in the last workgroup to finish, behind a
+//    device-scope fence, costs far more on this 8-XCD part: the fence writes
+//    back and invalidates the L2 of every workgroup's XCD.)
+//  * Page pipeline: each wave orders its next 64 pages (valid first, by tier)
+//    in registers, then keeps the loads of page k+1 in flight (a second
+//    register set) while page k is computed.
 #include "ska_internal.h"
 
 namespace ska {
@@ -82,6 +92,20 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&cw)[8], int i) {
     return __builtin_amdgcn_alignbit(cw[w + 1], cw[w], o) & mask;
 }
 
+// F + fp16(u half) * w in fp32 (v_fma_mix_f32).  Written as inline asm so
+// that the packed query halves stay packed in registers: the compiler would
+// otherwise hoist their conversion to fp32 out of the page loop.
+__device__ __forceinline__ float fma_mix_lo(uint32_t u, float w, float acc) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(u), "v"(w), "v"(acc));
+    return r;
+}
+__device__ __forceinline__ float fma_mix_hi(uint32_t u, float w, float acc) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(u), "v"(w), "v"(acc));
+    return r;
+}
+
 // Load the lane's slice of a record: SW dwords at byte address p (4-aligned).
 template <int SW>
 __device__ __forceinline__ void load_slice(const uint8_t *p, uint32_t (&cw)[8]) {
@@ -104,34 +128,72 @@ __device__ __forceinline__ void load_slice(const uint8_t *p, uint32_t (&cw)[8]) 
     }
 }
 
+
 struct WaveState {
     float m;     // running max (log2 units) of this lane's head
     float l;     // this lane's share of the softmax denominator
 };
 
-// One page of one kv head for one wave.
-template <int D, int G, int B>
-__device__ __forceinline__ void do_page(const DecodeArgs &A, const uint8_t *__restrict__ blk,
-                                        const uint16_t *__restrict__ vblk, const uint8_t *__restrict__ rblk,
-                                        int ntok, int64_t logit_base, const float (&u)[D / 4][G],
-                                        const float2 *__restrict__ lut, const float *__restrict__ rlev,
-                                        float *__restrict__ pb, WaveState &st, v4f (&acc)[D / 16]) {
-    constexpr int NA = D / 4;
+// Per-lane registers of one page: the lane's code slice, the radius byte of
+// its token, and its V fragments for the MFMA B operand.
+template <int D>
+struct PageBuf {
+    uint32_t cw[8];
+    uint32_t rc;
+    uint2 vf[D / 16];
+};
+
+// Wave-uniform description of one page.
+struct PageDesc {
+    int phys, b, p;
+    uint64_t off;   // byte offset of the physical page's code block
+};
+
+template <int D, int B>
+__device__ __forceinline__ void load_page_b(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
     constexpr int KB = record_bytes(D, B);
-    constexpr int SW = KB / 16;        // dwords per slice
+    constexpr int SW = KB / 16;
+    const int lane = threadIdx.x & 63;
+    const int t = lane >> 2, j = lane & 3;
+    const int q4 = lane >> 4, n16 = lane & 15;
+    const uint8_t *blk = A.kcode + pd.off + (uint64_t)kvh * kPage * KB;
+    load_slice<SW>(blk + t * KB + j * (KB / 4), r.cw);
+    const int64_t pk = (int64_t)pd.phys * A.hkv + kvh;
+    r.rc = A.rcode[pk * kPage + t];
+    const uint16_t *vblk = A.v + pk * (int64_t)D * kPage;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k)
+        r.vf[k] = *reinterpret_cast<const uint2 *>(vblk + (16 * k + n16) * kPage + 4 * q4);
+}
+
+template <int D, int TB>
+__device__ __forceinline__ void load_page(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
+    if constexpr (TB != 0) {
+        load_page_b<D, TB>(A, pd, kvh, r);
+    } else {
+        switch (pd.b) {
+            case 2: load_page_b<D, 2>(A, pd, kvh, r); break;
+            case 3: load_page_b<D, 3>(A, pd, kvh, r); break;
+            case 4: load_page_b<D, 4>(A, pd, kvh, r); break;
+            case 6: load_page_b<D, 6>(A, pd, kvh, r); break;
+            default: load_page_b<D, 8>(A, pd, kvh, r); break;
+        }
+    }
+}
+
+// f_b, logits, online softmax and the MFMA P.V update of one page.  DBG also
+// stores the logits (a separate kernel variant, so that the store does not
+// enter the memory-wait accounting of the production loop).
+template <int D, int G, int B, bool DBG>
+__device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &r, int ntok, int64_t logit_base,
+                                               const uint32_t (&u)[D * G / 8], float sq, const float2 *__restrict__ lut,
+                                               const float *__restrict__ rlev, float *__restrict__ pb,
+                                               WaveState &st, v4f (&acc)[D / 16]) {
+    constexpr int NA = D / 4;
     constexpr int NT = D / 16;
     const int lane = threadIdx.x & 63;
     const int t = lane >> 2, j = lane & 3;
     const int q4 = lane >> 4, n16 = lane & 15;
-
-    // ---- loads: codes (the lane's slice), radius byte, V fragments ----
-    uint32_t cw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    load_slice<SW>(blk + t * KB + j * (KB / 4), cw);
-    const int rc = rblk[t];
-    uint2 vf[NT];
-#pragma unroll
-    for (int k = 0; k < NT; ++k)
-        vf[k] = *reinterpret_cast<const uint2 *>(vblk + (16 * k + n16) * kPage + 4 * q4);
 
     // ---- f_b on the lane's slice ----
     const int az_base = (j == 3) ? lut_azimuth(B) : lut_polar(B);
@@ -142,7 +204,7 @@ __device__ __forceinline__ void do_page(const DecodeArgs &A, const uint8_t *__re
     float P = 1.f;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        const uint32_t c = code_at<B>(cw, i);
+        const uint32_t c = code_at<B>(r.cw, i);
         int e;
         if (i == NA - 2) e = az_base + (int)c;
         else if (i == NA - 1) e = pad_base + (int)c;
@@ -151,7 +213,10 @@ __device__ __forceinline__ void do_page(const DecodeArgs &A, const uint8_t *__re
         const float w = P * cs.x;
         P = P * cs.y;
 #pragma unroll
-        for (int h = 0; h < G; ++h) F[h] = fmaf(u[i][h], w, F[h]);
+        for (int h = 0; h < G; ++h) {
+            const int e2 = i * G + h;   // element (angle i, head h) of the packed halves
+            F[h] = (e2 & 1) ? fma_mix_hi(u[e2 >> 1], w, F[h]) : fma_mix_lo(u[e2 >> 1], w, F[h]);
+        }
     }
 
     // ---- join the four slices: C_j = prod_{i<j} S_i ----
@@ -187,8 +252,10 @@ __device__ __forceinline__ void do_page(const DecodeArgs &A, const uint8_t *__re
     }
 
     // ---- logits (log2 units) and online softmax ----
-    const float lg = (t < ntok) ? rlev[rc] * f : -INFINITY;
-    if (A.logits && j < G && t < ntok) A.logits[logit_base + (int64_t)j * A.max_pages * kPage + t] = lg * kLn2;
+    const float lg = (t < ntok) ? sq * rlev[r.rc] * f : -INFINITY;
+    if constexpr (DBG) {
+        if (j < G && t < ntok) A.logits[logit_base + (int64_t)j * A.max_pages * kPage + t] = lg * kLn2;
+    }
     if (__builtin_amdgcn_ballot_w64(lg > st.m + 8.f) != 0ull) {
         const float pm = head_reduce<G, true>(lg);
         const float mn = fmaxf(st.m, pm);
@@ -213,15 +280,15 @@ __device__ __forceinline__ void do_page(const DecodeArgs &A, const uint8_t *__re
         const float4 pv = *reinterpret_cast<const float4 *>(pb + (n16 % G) * 16 + 4 * q4);
         const bool lo = n16 >= G;
         const float pr[4] = {pv.x, pv.y, pv.z, pv.w};
-        short s[4];
+        short sh[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t bits = __float_as_uint(pr[i]);
             const float hi = __uint_as_float(bits & 0xFFFF0000u);
             const float x = lo ? (pr[i] - hi) : pr[i];
-            s[i] = (short)(__float_as_uint(x) >> 16);
+            sh[i] = (short)(__float_as_uint(x) >> 16);
         }
-        af = v4s{s[0], s[1], s[2], s[3]};
+        af = v4s{sh[0], sh[1], sh[2], sh[3]};
     }
     if (ntok < kPage) {
         // zero the values of tokens past the end (the page tail may hold anything)
@@ -229,24 +296,58 @@ __device__ __forceinline__ void do_page(const DecodeArgs &A, const uint8_t *__re
         const uint32_t m0 = (base + 0 < ntok ? 0x0000FFFFu : 0u) | (base + 1 < ntok ? 0xFFFF0000u : 0u);
         const uint32_t m1 = (base + 2 < ntok ? 0x0000FFFFu : 0u) | (base + 3 < ntok ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int k = 0; k < NT; ++k) { vf[k].x &= m0; vf[k].y &= m1; }
+        for (int k = 0; k < NT; ++k) { r.vf[k].x &= m0; r.vf[k].y &= m1; }
     }
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
         v4s bfr;
-        __builtin_memcpy(&bfr, &vf[k], 8);
+        __builtin_memcpy(&bfr, &r.vf[k], 8);
         acc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(af, bfr, acc[k], 0, 0, 0);
     }
 }
 
+template <int D, int G, int TB, bool DBG>
+__device__ __forceinline__ void compute_page(const DecodeArgs &A, const PageDesc &pd, PageBuf<D> &r, int len,
+                                             int64_t head0, const uint32_t (&u)[D * G / 8], float sq,
+                                             const float2 *__restrict__ lut, const float *__restrict__ rlev,
+                                             float *__restrict__ pb, WaveState &st, v4f (&acc)[D / 16]) {
+    const int ntok = min(kPage, len - pd.p * kPage);
+    const int64_t lbase = head0 * A.max_pages * kPage + (int64_t)pd.p * kPage;
+    if constexpr (TB != 0) {
+        compute_page_b<D, G, TB, DBG>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc);
+    } else {
+        switch (pd.b) {
+            case 2: compute_page_b<D, G, 2, DBG>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
+            case 3: compute_page_b<D, G, 3, DBG>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
+            case 4: compute_page_b<D, G, 4, DBG>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
+            case 6: compute_page_b<D, G, 6, DBG>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
+            default: compute_page_b<D, G, 8, DBG>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
+        }
+    }
+}
+
+// The lane's packed query halves for one tier, from global memory (single
+// tier, once per workgroup) or from the workgroup's LDS copy (mixed tiers).
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs A) {
+__device__ __forceinline__ void load_query(const uint4 *src, uint32_t (&u)[D * G / 8]) {
+    constexpr int NW = D * G / 8;   // packed words per lane: (d/4) angles x G heads / 2
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+        const uint4 x = src[i];
+        u[4 * i + 0] = x.x; u[4 * i + 1] = x.y; u[4 * i + 2] = x.z; u[4 * i + 3] = x.w;
+    }
+}
+
+// TB: the angle bit width of every page when the pool has a single tier, or 0
+// (pages of mixed tiers, dispatched per page on the header).
+template <int D, int G, int TB, bool DBG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_decode(DecodeArgs A) {
     constexpr int NA = D / 4;
     constexpr int NT = D / 16;
     const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int j = lane & 3;
     const int q4 = lane >> 4, n16 = lane & 15;
+    const int64_t head0 = (int64_t)seq * A.hq + (int64_t)kvh * G;
 
     int len = A.seq_lens[seq];
     len = max(0, min(len, A.max_pages * kPage));
@@ -260,34 +361,51 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs A) {
     __shared__ __attribute__((aligned(16))) float pbuf[kWaves][G * 16];
     __shared__ float mo[kWaves][2 * G][D];
     __shared__ float mml[kWaves][G][2];
+    // query halves of every tier present (mixed-tier pools only)
+    __shared__ __attribute__((aligned(16))) uint32_t uq_lds[TB == 0 ? 5 * D * G / 2 : 4];
 
-    for (int e = tid; e < kLutEntries; e += kThreads) lut[e] = A.lut[e];
+    if constexpr (TB != 0) {
+        // only this tier's tables and the (1, 1) padding entries it can index
+        for (int e = tid; e < 2 << TB; e += kThreads) lut[lut_polar(TB) + e] = A.lut[lut_polar(TB) + e];
+        for (int e = tid; e < 1 << TB; e += kThreads) lut[kLutOnes + e] = A.lut[kLutOnes + e];
+    } else {
+        for (int e = tid; e < kLutEntries; e += kThreads) lut[e] = A.lut[e];
+    }
     rlev[tid] = A.rlev[kvh * 256 + tid];
+    const uint32_t *uq_glb = reinterpret_cast<const uint32_t *>(A.uq + ((int64_t)seq * A.hkv + kvh) * A.nt * D * G);
+    if constexpr (TB == 0)
+        for (int e = tid; e < A.nt * D * G / 2; e += kThreads) uq_lds[e] = uq_glb[e];
     __syncthreads();
 
     const int ppw = A.pps / kWaves;
     const int wp0 = p0 + wave * ppw;
     const int wp1 = min(wp0 + ppw, p1);
-    const bool mixed = __builtin_popcount(A.tier_mask) > 1;
 
     WaveState st{-INFINITY, 0.f};
     v4f acc[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) acc[k] = v4f{0.f, 0.f, 0.f, 0.f};
-    float u[NA][G];
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-#pragma unroll
-        for (int h = 0; h < G; ++h) u[i][h] = 0.f;
+    uint32_t u[D * G / 8];
     int cur_b = -1;
+    const int jq = lane & 3;
+    if constexpr (TB != 0) {
+        load_query<D, G>(reinterpret_cast<const uint4 *>(uq_glb + (A.tslot[TB] * 4 + jq) * (D * G / 8)), u);
+        cur_b = TB;
+    } else {
+#pragma unroll
+        for (int i = 0; i < D * G / 8; ++i) u[i] = 0u;
+    }
+    // this lane's head in the softmax: j % G
+    const float sq = A.sq[head0 + ((lane & 3) % G)];
 
     const int64_t bt_row = (int64_t)seq * A.max_pages;
-    const int64_t head0 = (int64_t)seq * A.hq + (int64_t)kvh * G;
     float *pb = pbuf[wave];
 
     for (int c0 = wp0; c0 < wp1; c0 += 64) {
         const int cn = min(64, wp1 - c0);
-        // this chunk's page list: lane i holds page c0 + i
+        // this chunk's page list, one page per lane, valid pages first
+        // (ordered by tier when tiers are mixed, so that the query registers
+        // change at most once per tier)
         int e_pg = c0 + lane, e_phys = -1, e_bits = 0;
         uint32_t e_lo = 0, e_hi = 0;
         if (lane < cn) {
@@ -305,53 +423,63 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs A) {
                 e_hi = (uint32_t)(off >> 32);
             }
         }
-        if (mixed) {
-            // stable sort of the chunk by tier, so that the query registers
-            // change at most once per tier
-            const int key = (lane < cn) ? e_bits : 15;
-            const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-            int rank = 0;
-            for (int v = 0; v <= 15; ++v) {
-                const uint64_t bal = __builtin_amdgcn_ballot_w64(key == v);
-                if (bal == 0ull) continue;
-                if (v < key) rank += __popcll(bal);
-                else if (v == key) rank += __popcll(bal & lt);
-            }
-            e_pg = __builtin_amdgcn_ds_permute(rank * 4, e_pg);
-            e_phys = __builtin_amdgcn_ds_permute(rank * 4, e_phys);
-            e_bits = __builtin_amdgcn_ds_permute(rank * 4, e_bits);
-            e_lo = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)e_lo);
-            e_hi = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)e_hi);
-        }
-        for (int k = 0; k < cn; ++k) {
-            const int phys = __builtin_amdgcn_readlane(e_phys, k);
-            if (phys < 0) continue;
-            const int b = __builtin_amdgcn_readlane(e_bits, k);
-            const int p = __builtin_amdgcn_readlane(e_pg, k);
-            const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)e_hi, k) << 32) |
-                                 (uint32_t)__builtin_amdgcn_readlane((int)e_lo, k);
-            const int ntok = min(kPage, len - p * kPage);
-            if (b != cur_b) {
-                const float4 *src = reinterpret_cast<const float4 *>(
-                    A.uq + ((((int64_t)seq * A.hkv + kvh) * A.nt + A.tslot[b]) * 4 + j) * (NA * G));
-                float *ud = &u[0][0];
+        const int key = (e_phys >= 0) ? e_bits : 15;
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int rank = 0, nvalid = 0;
+        constexpr int kKeys[6] = {2, 3, 4, 6, 8, 15};
 #pragma unroll
-                for (int i = 0; i < NA * G / 4; ++i) {
-                    const float4 x = src[i];
-                    ud[4 * i + 0] = x.x; ud[4 * i + 1] = x.y; ud[4 * i + 2] = x.z; ud[4 * i + 3] = x.w;
+        for (int vi = 0; vi < 6; ++vi) {
+            const int v = kKeys[vi];
+            if (TB != 0 && v != TB && v != 15) continue;
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(key == v);
+            if (v < key) rank += __popcll(bal);
+            else if (v == key) rank += __popcll(bal & lt);
+            if (v != 15) nvalid += __popcll(bal);
+        }
+        e_pg = __builtin_amdgcn_ds_permute(rank * 4, e_pg);
+        e_phys = __builtin_amdgcn_ds_permute(rank * 4, e_phys);
+        e_bits = __builtin_amdgcn_ds_permute(rank * 4, e_bits);
+        e_lo = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)e_lo);
+        e_hi = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)e_hi);
+        if (nvalid == 0) continue;
+
+        auto desc = [&](int k) {
+            PageDesc pd;
+            pd.phys = __builtin_amdgcn_readlane(e_phys, k);
+            pd.b = TB != 0 ? TB : __builtin_amdgcn_readlane(e_bits, k);
+            pd.p = __builtin_amdgcn_readlane(e_pg, k);
+            pd.off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)e_hi, k) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)e_lo, k);
+            return pd;
+        };
+        auto ensure_query = [&](int b) {
+            if constexpr (TB == 0) {
+                if (b != cur_b) {
+                    load_query<D, G>(reinterpret_cast<const uint4 *>(uq_lds + (A.tslot[b] * 4 + jq) * (D * G / 8)), u);
+                    cur_b = b;
                 }
-                cur_b = b;
             }
-            const int64_t pk = (int64_t)phys * A.hkv + kvh;
-            const uint16_t *vblk = A.v + pk * (int64_t)D * kPage;
-            const uint8_t *rblk = A.rcode + pk * kPage;
-            const int64_t lbase = head0 * A.max_pages * kPage + (int64_t)p * kPage;
-            switch (b) {
-                case 2: do_page<D, G, 2>(A, A.kcode + off + (uint64_t)kvh * kPage * record_bytes(D, 2), vblk, rblk, ntok, lbase, u, lut, rlev, pb, st, acc); break;
-                case 3: do_page<D, G, 3>(A, A.kcode + off + (uint64_t)kvh * kPage * record_bytes(D, 3), vblk, rblk, ntok, lbase, u, lut, rlev, pb, st, acc); break;
-                case 4: do_page<D, G, 4>(A, A.kcode + off + (uint64_t)kvh * kPage * record_bytes(D, 4), vblk, rblk, ntok, lbase, u, lut, rlev, pb, st, acc); break;
-                case 6: do_page<D, G, 6>(A, A.kcode + off + (uint64_t)kvh * kPage * record_bytes(D, 6), vblk, rblk, ntok, lbase, u, lut, rlev, pb, st, acc); break;
-                default: do_page<D, G, 8>(A, A.kcode + off + (uint64_t)kvh * kPage * record_bytes(D, 8), vblk, rblk, ntok, lbase, u, lut, rlev, pb, st, acc); break;
+        };
+        // two register sets: the loads of page k+1 are in flight while page k
+        // is computed.  The loads are issued unconditionally (past the end
+        // they repeat the last page) so that the wait before each compute
+        // only covers the loads of the page being computed.
+        PageBuf<D> R0, R1;
+        const int last = nvalid - 1;
+        PageDesc d0 = desc(0);
+        load_page<D, TB>(A, d0, kvh, R0);
+        for (int k = 0; k < nvalid; k += 2) {
+            const PageDesc d1 = desc(min(k + 1, last));
+            load_page<D, TB>(A, d1, kvh, R1);
+            __builtin_amdgcn_sched_barrier(0);   // issue these loads before waiting on page k
+            ensure_query(d0.b);
+            compute_page<D, G, TB, DBG>(A, d0, R0, len, head0, u, sq, lut, rlev, pb, st, acc);
+            d0 = desc(min(k + 2, last));
+            load_page<D, TB>(A, d0, kvh, R0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (k + 1 < nvalid) {
+                ensure_query(d1.b);
+                compute_page<D, G, TB, DBG>(A, d1, R1, len, head0, u, sq, lut, rlev, pb, st, acc);
             }
         }
     }
@@ -367,8 +495,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs A) {
         const float a4[4] = {acc[k].x, acc[k].y, acc[k].z, acc[k].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = 4 * q4 + i;
-            if (r < 2 * G) mo[wave][r][16 * k + n16] = a4[i];
+            const int rr = 4 * q4 + i;
+            if (rr < 2 * G) mo[wave][rr][16 * k + n16] = a4[i];
         }
     }
     __syncthreads();
@@ -393,54 +521,76 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs A) {
             A.part_ml[2 * pi + 1] = L;
         }
     }
+
 }
 
+// Split merge: one workgroup of d threads per (sequence, query head):
+// M = max_s m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  The
+// (m, l) pairs are wave-uniform (scalar loads); the o_s loads of a thread
+// are independent and unrolled.  A sequence with no resident token gets 0.
 template <int D>
-__global__ __launch_bounds__(128) void k_merge(MergeArgs A) {
-    const int seq = blockIdx.x / A.hq;
+__global__ __launch_bounds__(D) void k_merge(MergeArgs A) {
+    const int row = blockIdx.x;
+    const int seq = row / A.hq;
     const int e = threadIdx.x;
-    const int64_t row = blockIdx.x;
     int len = A.seq_lens[seq];
     len = max(0, min(len, A.max_pages * kPage));
     const int npages = (len + kPage - 1) / kPage;
     const int ns = (npages + A.pps - 1) / A.pps;
-    const float *ml = A.part_ml + row * A.nsplit * 2;
-    const float *po = A.part_o + row * A.nsplit * D;
+    const float *ml = A.part_ml + (int64_t)row * A.nsplit * 2;
+    const float *po = A.part_o + (int64_t)row * A.nsplit * D + e;
     float M = -INFINITY;
     for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-    float out = 0.f;
+    float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
-        float L = 0.f, O = 0.f;
+#pragma unroll 8
         for (int s = 0; s < ns; ++s) {
             const float sc = exp2f(ml[2 * s] - M);
             L += sc * ml[2 * s + 1];
-            O += sc * po[(int64_t)s * D + e];
+            O += sc * po[(int64_t)s * D];
         }
-        out = O / L;
     }
-    A.out[row * D + e] = out;
+    A.out[(int64_t)row * D + e] = (M != -INFINITY) ? O / L : 0.f;
+}
+
+template <int D, int G>
+static void launch_dg(const DecodeArgs &a, int tb, dim3 grid, hipStream_t s) {
+    if (a.logits) {  // debug variant: stores the logits; generic tier dispatch
+        hipLaunchKernelGGL((k_decode<D, G, 0, true>), grid, dim3(kThreads), 0, s, a);
+        return;
+    }
+    switch (tb) {
+        case 2: hipLaunchKernelGGL((k_decode<D, G, 2, false>), grid, dim3(kThreads), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((k_decode<D, G, 3, false>), grid, dim3(kThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((k_decode<D, G, 4, false>), grid, dim3(kThreads), 0, s, a); break;
+        case 6: hipLaunchKernelGGL((k_decode<D, G, 6, false>), grid, dim3(kThreads), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((k_decode<D, G, 8, false>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((k_decode<D, G, 0, false>), grid, dim3(kThreads), 0, s, a); break;
+    }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s) {
     if (B == 0) return hipSuccess;
-    const dim3 grid((unsigned)a.nsplit, (unsigned)a.hkv, (unsigned)B), block(kThreads);
+    const dim3 grid((unsigned)a.nsplit, (unsigned)a.hkv, (unsigned)B);
+    int tb = 0;
+    if (__builtin_popcount(a.tier_mask) == 1) tb = __builtin_ctz(a.tier_mask);
     if (d == 128) {
-        if (G == 4) hipLaunchKernelGGL((k_decode<128, 4>), grid, block, 0, s, a);
-        else if (G == 2) hipLaunchKernelGGL((k_decode<128, 2>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_decode<128, 1>), grid, block, 0, s, a);
+        if (G == 4) launch_dg<128, 4>(a, tb, grid, s);
+        else if (G == 2) launch_dg<128, 2>(a, tb, grid, s);
+        else launch_dg<128, 1>(a, tb, grid, s);
     } else {
-        if (G == 4) hipLaunchKernelGGL((k_decode<64, 4>), grid, block, 0, s, a);
-        else if (G == 2) hipLaunchKernelGGL((k_decode<64, 2>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_decode<64, 1>), grid, block, 0, s, a);
+        if (G == 4) launch_dg<64, 4>(a, tb, grid, s);
+        else if (G == 2) launch_dg<64, 2>(a, tb, grid, s);
+        else launch_dg<64, 1>(a, tb, grid, s);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs &a, int B, hipStream_t s) {
     if (B == 0) return hipSuccess;
-    const dim3 grid((unsigned)(B * a.hq)), block((unsigned)a.d);
-    if (a.d == 128) hipLaunchKernelGGL(k_merge<128>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(k_merge<64>, grid, block, 0, s, a);
+    const dim3 grid((unsigned)(B * a.hq));
+    if (a.d == 128) hipLaunchKernelGGL(k_merge<128>, grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL(k_merge<64>, grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -238,7 +238,7 @@ ska_status calibrate(ska_cache *c, const float *keys, int64_t n, hipStream_t s) 
     return set_range(c, range.data());
 }
 
-ska_status ensure_ws(ska_cache *c, size_t bytes) {
+ska_status ensure_ws(ska_cache *c, size_t bytes, hipStream_t s) {
     if (bytes <= c->ws_bytes) return SKA_OK;
     if (c->d_ws) {
         if (hipFree(c->d_ws) != hipSuccess) return SKA_ERR_HIP;  // hipFree waits for work using it
@@ -357,14 +357,18 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     const int nsplit = (max_pages + pps - 1) / pps;
     if ((int64_t)nsplit * hkv > (1ll << 31) || batch > 65535 || nsplit > (1 << 30)) return SKA_ERR_UNSUPPORTED;
 
+    // workspace: [query scales | query directions (fp16) | partial o | partial (m, l)]
+    const size_t sq_n = (size_t)batch * num_q_heads;
     const size_t uq_n = (size_t)batch * hkv * c->nt * d * G;
     const size_t po_n = (size_t)batch * num_q_heads * nsplit * d;
     const size_t pm_n = (size_t)batch * num_q_heads * nsplit * 2;
-    const size_t off_po = align256(uq_n * 4), off_pm = off_po + align256(po_n * 4);
-    ska_status st = ensure_ws(c, off_pm + align256(pm_n * 4));
+    const size_t off_sq = 0;
+    const size_t off_uq = off_sq + align256(sq_n * 4);
+    const size_t off_po = off_uq + align256(uq_n * 2), off_pm = off_po + align256(po_n * 4);
+    hipStream_t s = (hipStream_t)stream;
+    ska_status st = ensure_ws(c, off_pm + align256(pm_n * 4), s);
     if (st != SKA_OK) return st;
     char *ws = (char *)c->d_ws;
-    hipStream_t s = (hipStream_t)stream;
     hipEvent_t *ev = nullptr;
     if (c->prof_n < c->prof_max) ev = &c->prof_ev[4 * (size_t)c->prof_n++];
     if (ev && hipEventRecord(ev[0], s) != hipSuccess) return SKA_ERR_HIP;
@@ -381,7 +385,8 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     qa.query_mode = c->pool.query_mode;
     qa.scale = scale;
     qa.tab = CodeTables{c->d_cos2, c->d_sin2, c->d_cen};
-    qa.uq = (float *)ws;
+    qa.uq = (_Float16 *)(ws + off_uq);
+    qa.sq = (float *)(ws + off_sq);
     if (launch_qprep(qa, s) != hipSuccess) return SKA_ERR_HIP;
     if (ev && hipEventRecord(ev[1], s) != hipSuccess) return SKA_ERR_HIP;
 
@@ -393,7 +398,8 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     da.page_bits = c->pool.page_bits;
     da.block_table = block_table;
     da.seq_lens = seq_lens;
-    da.uq = (const float *)ws;
+    da.uq = (const _Float16 *)(ws + off_uq);
+    da.sq = (const float *)(ws + off_sq);
     da.lut = c->d_lut;
     da.rlev = c->d_rlev;
     da.part_o = (float *)(ws + off_po);
@@ -425,6 +431,7 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     ma.nsplit = nsplit;
     if (launch_merge(ma, batch, s) != hipSuccess) return SKA_ERR_HIP;
     if (ev && hipEventRecord(ev[3], s) != hipSuccess) return SKA_ERR_HIP;
+
     return SKA_OK;
 }
 

@@ -66,7 +66,8 @@ struct QPrepArgs {
     int query_mode;
     float scale;             // softmax scale
     CodeTables tab;
-    float *uq;               // [B][hkv][nt][4][d/4][G]
+    _Float16 *uq;            // [B][hkv][nt][4][d/4][G] unit query directions
+    float *sq;               // [B][hq] scale * |q| * log2(e)
 };
 
 struct DecodeArgs {
@@ -77,7 +78,8 @@ struct DecodeArgs {
     const uint8_t *page_bits;
     const int32_t *block_table;
     const int32_t *seq_lens;
-    const float *uq;
+    const _Float16 *uq;      // [B][hkv][nt][4][d/4][G]
+    const float *sq;         // [B][hq]
     const float2 *lut;       // [kLutEntries]
     const float *rlev;       // [hkv][256] radius levels
     float *part_o;           // [B][hq][nsplit][d]
@@ -94,6 +96,13 @@ struct DecodeArgs {
     int8_t tslot[9];         // tier b -> index among the tiers present
 };
 
+
+hipError_t launch_calibrate(const float *keys, int64_t n, int hkv, int d, unsigned long long *minmax,
+                            hipStream_t s);
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
+hipError_t launch_qprep(const QPrepArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s);
+
 struct MergeArgs {
     const float *part_o;
     const float *part_ml;
@@ -101,12 +110,6 @@ struct MergeArgs {
     float *out;
     int hq, d, max_pages, pps, nsplit;
 };
-
-hipError_t launch_calibrate(const float *keys, int64_t n, int hkv, int d, unsigned long long *minmax,
-                            hipStream_t s);
-hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
-hipError_t launch_qprep(const QPrepArgs &a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, int B, hipStream_t s);
 
 }  // namespace ska

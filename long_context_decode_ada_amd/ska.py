@@ -200,7 +200,7 @@ def profile_begin(cache: Cache, max_calls: int):
 
 
 def profile_read(cache: Cache, max_calls: int) -> np.ndarray:
-    """[calls][3] kernel milliseconds (query prep, decode, merge)."""
+    """[calls][3] kernel milliseconds (query prep, decode, split merge)."""
     ms = np.zeros((max(1, max_calls), 3), np.float32)
     n = ctypes.c_int(0)
     _check(lib().ska_profile_read(cache.handle, ms.ctypes.data_as(ctypes.c_void_p), int(max_calls),

@@ -70,6 +70,7 @@ def test_split_count_and_determinism():
             base = g
         else:
             assert np.array_equal(g["logits"], base["logits"], equal_nan=True)
+            assert np.array_equal(g["out"], g["out_dbg"]) or np.abs(g["out"] - g["out_dbg"]).max() < 1e-6
             assert np.abs(g["out"] - base["out"]).max() < 1e-5
 
 
