@@ -148,10 +148,10 @@ ska_status ska_device_errors(ska_cache *cache, void *stream, uint32_t *flags_out
  * and kernel-realised throughput on the paged substrate) and section 4
  * ("kernel-realised efficiency"): ska_profile_begin makes the next
  * `max_calls` ska_decode_attention calls on this cache record HIP events on
- * their stream around each of their three kernels (query preparation, paged
- * decode, split merge); 0 stops recording.  ska_profile_read waits for the
- * recorded events and writes ms_out[i*3 + k] for call i and kernel k,
- * *n_out = calls recorded (at most max_calls). */
+ * their stream around each of their two kernels (the paged decode, which
+ * also prepares the query codes, and the split merge); 0 stops recording.
+ * ska_profile_read waits for the recorded events and writes ms_out[i*2 + k]
+ * for call i and kernel k, *n_out = calls recorded (at most max_calls). */
 ska_status ska_profile_begin(ska_cache *cache, int max_calls);
 ska_status ska_profile_read(ska_cache *cache, float *ms_out, int max_calls, int *n_out);
 

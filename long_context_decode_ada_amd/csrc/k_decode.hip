@@ -22,7 +22,8 @@
 //    product scan of the slice sine products (DPP quad permutes):
 //    f_h = sum_j C_j F_h,j with C_j = prod_{i<j} S_i.
 //  * The query side, the unit vector uq = u(centres(c_q)) per tier, is
-//    prepared once per step (k_qprep) as fp16 pairs and held packed in
+//    prepared in each workgroup's prologue (from the G query rows of its kv
+//    head: exact codes, then a product scan) as fp16 pairs and held packed in
 //    registers; v_fma_mix_f32 multiplies a half by the fp32 w and accumulates
 //    in fp32.  Rounding uq to fp16 moves f by at most 2^-11 (Cauchy-Schwarz
 //    over two unit vectors).  The logit is sq_h * r~ * f with
@@ -44,6 +45,7 @@
 //  * Page pipeline: each wave orders its next 64 pages (valid first, by tier)
 //    in registers, then keeps the loads of page k+1 in flight (a second
 //    register set) while page k is computed.
+#include "ska_codes.h"
 #include "ska_internal.h"
 
 namespace ska {
@@ -92,6 +94,58 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&cw)[8], int i) {
     return __builtin_amdgcn_alignbit(cw[w + 1], cw[w], o) & mask;
 }
 
+// 8 * (code i) of a slice: the byte offset of its (cos, sin) entry.  For
+// b = 4, 8 and 2 the codes of each word are first spread (two or four masked
+// shifts per word) so that every 8*code sits in its own byte or half-word and
+// takes one extraction; other widths use a field extract and a shift.
+template <int B>
+struct CodeAddr {
+    uint32_t s[16];
+    __device__ __forceinline__ void init(const uint32_t (&cw)[8]) {
+        constexpr int SW = record_bytes(B == 3 ? 128 : 128, B) / 16;
+        if constexpr (B == 4) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                s[2 * k + 0] = (cw[k] & 0x0F0F0F0Fu) << 3;     // even codes * 8, one per byte
+                s[2 * k + 1] = (cw[k] >> 1) & 0x78787878u;     // odd codes * 8
+            }
+        } else if constexpr (B == 8) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                s[2 * k + 0] = (cw[k] & 0x00FF00FFu) << 3;     // codes 0, 2 of the word, one per half-word
+                s[2 * k + 1] = (cw[k] >> 5) & 0x07F807F8u;     // codes 1, 3
+            }
+        } else if constexpr (B == 2) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) s[4 * k + m] = ((cw[k] >> (2 * m)) & 0x03030303u) << 3;
+        }
+        if constexpr (B == 2 || B == 4 || B == 8) {
+            // keep the spread words as computed: folded back into the code
+            // words, each extraction would again cost a shift and a mask
+            constexpr int NS = (B == 8) ? 16 : 8;
+#pragma unroll
+            for (int k = 0; k < NS; ++k) asm volatile("" : "+v"(s[k]));
+        }
+        (void)SW;
+    }
+    __device__ __forceinline__ uint32_t at(const uint32_t (&cw)[8], int i) const {
+        if constexpr (B == 4) {
+            const uint32_t w = s[2 * (i >> 3) + (i & 1)];
+            return __builtin_amdgcn_ubfe(w, 8 * ((i & 7) >> 1), 8);
+        } else if constexpr (B == 8) {
+            const uint32_t w = s[2 * (i >> 2) + (i & 1)];
+            return __builtin_amdgcn_ubfe(w, 16 * ((i & 3) >> 1), 16);
+        } else if constexpr (B == 2) {
+            const uint32_t w = s[4 * (i >> 4) + (i & 3)];
+            return __builtin_amdgcn_ubfe(w, 8 * ((i & 15) >> 2), 8);
+        } else {
+            return code_at<B>(cw, i) << 3;
+        }
+    }
+};
+
 // F + fp16(u half) * w in fp32 (v_fma_mix_f32).  Written as inline asm so
 // that the packed query halves stay packed in registers: the compiler would
 // otherwise hoist their conversion to fp32 out of the page loop.
@@ -105,29 +159,6 @@ __device__ __forceinline__ float fma_mix_hi(uint32_t u, float w, float acc) {
     asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(u), "v"(w), "v"(acc));
     return r;
 }
-
-// Load the lane's slice of a record: SW dwords at byte address p (4-aligned).
-template <int SW>
-__device__ __forceinline__ void load_slice(const uint8_t *p, uint32_t (&cw)[8]) {
-    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-    if constexpr (SW % 4 == 0) {
-#pragma unroll
-        for (int k = 0; k < SW / 4; ++k) {
-            const uint4 x = *reinterpret_cast<const uint4 *>(q + 4 * k);
-            cw[4 * k + 0] = x.x; cw[4 * k + 1] = x.y; cw[4 * k + 2] = x.z; cw[4 * k + 3] = x.w;
-        }
-    } else if constexpr (SW % 2 == 0) {
-#pragma unroll
-        for (int k = 0; k < SW / 2; ++k) {
-            const uint2 x = *reinterpret_cast<const uint2 *>(q + 2 * k);
-            cw[2 * k + 0] = x.x; cw[2 * k + 1] = x.y;
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < SW; ++k) cw[k] = q[k];
-    }
-}
-
 
 struct WaveState {
     float m;     // running max (log2 units) of this lane's head
@@ -149,6 +180,15 @@ struct PageDesc {
     uint64_t off;   // byte offset of the physical page's code block
 };
 
+// Raw buffer descriptor (V#) over `bytes` bytes at a wave-uniform address:
+// loads past the end return 0 instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Loads of one page: the page's code block, radius bytes and V block each
+// get a descriptor built in scalar registers; the per-lane offsets inside a
+// block are the same for every page.
 template <int D, int B>
 __device__ __forceinline__ void load_page_b(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
     constexpr int KB = record_bytes(D, B);
@@ -156,14 +196,37 @@ __device__ __forceinline__ void load_page_b(const DecodeArgs &A, const PageDesc 
     const int lane = threadIdx.x & 63;
     const int t = lane >> 2, j = lane & 3;
     const int q4 = lane >> 4, n16 = lane & 15;
-    const uint8_t *blk = A.kcode + pd.off + (uint64_t)kvh * kPage * KB;
-    load_slice<SW>(blk + t * KB + j * (KB / 4), r.cw);
     const int64_t pk = (int64_t)pd.phys * A.hkv + kvh;
-    r.rc = A.rcode[pk * kPage + t];
-    const uint16_t *vblk = A.v + pk * (int64_t)D * kPage;
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + pd.off + (uint64_t)kvh * kPage * KB, kPage * KB);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(A.v + pk * (int64_t)D * kPage, D * kPage * 2);
+    const __amdgpu_buffer_rsrc_t rr = buf_rsrc(A.rcode + pk * kPage, kPage);
+    const int vo = t * KB + j * (KB / 4);
+    if constexpr (SW == 1) {
+        r.cw[0] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo, 0, 0);
+    } else if constexpr (SW == 2) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rk, vo, 0, 0);
+        r.cw[0] = x[0]; r.cw[1] = x[1];
+    } else if constexpr (SW == 3) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b96(rk, vo, 0, 0);
+        r.cw[0] = x[0]; r.cw[1] = x[1]; r.cw[2] = x[2];
+    } else {
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k)
-        r.vf[k] = *reinterpret_cast<const uint2 *>(vblk + (16 * k + n16) * kPage + 4 * q4);
+        for (int k = 0; k < SW / 4; ++k) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 16 * k, 0, 0);
+            r.cw[4 * k + 0] = x[0]; r.cw[4 * k + 1] = x[1]; r.cw[4 * k + 2] = x[2]; r.cw[4 * k + 3] = x[3];
+        }
+        if constexpr (SW % 4 == 2) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b64(rk, vo + 16 * (SW / 4), 0, 0);
+            r.cw[SW - 2] = x[0]; r.cw[SW - 1] = x[1];
+        }
+    }
+    r.rc = __builtin_amdgcn_raw_buffer_load_b8(rr, t, 0, 0);
+    const int vv = (n16 * kPage + 4 * q4) * 2;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rv, vv + k * 16 * kPage * 2, 0, 0);
+        r.vf[k] = make_uint2(x[0], x[1]);
+    }
 }
 
 template <int D, int TB>
@@ -196,20 +259,23 @@ __device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &
     const int q4 = lane >> 4, n16 = lane & 15;
 
     // ---- f_b on the lane's slice ----
-    const int az_base = (j == 3) ? lut_azimuth(B) : lut_polar(B);
-    const int pad_base = (j == 3) ? kLutOnes : lut_polar(B);
+    const uint32_t az_base = 8u * ((j == 3) ? lut_azimuth(B) : lut_polar(B));
+    const uint32_t pad_base = 8u * ((j == 3) ? kLutOnes : lut_polar(B));
+    const char *lutb = reinterpret_cast<const char *>(lut);
+    CodeAddr<B> ca;
+    ca.init(r.cw);
     float F[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) F[h] = 0.f;
     float P = 1.f;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        const uint32_t c = code_at<B>(r.cw, i);
-        int e;
-        if (i == NA - 2) e = az_base + (int)c;
-        else if (i == NA - 1) e = pad_base + (int)c;
-        else e = lut_polar(B) + (int)c;
-        const float2 cs = lut[e];
+        const uint32_t c8 = ca.at(r.cw, i);
+        uint32_t e8;
+        if (i == NA - 2) e8 = az_base + c8;
+        else if (i == NA - 1) e8 = pad_base + c8;
+        else e8 = 8u * lut_polar(B) + c8;
+        const float2 cs = *reinterpret_cast<const float2 *>(lutb + e8);
         const float w = P * cs.x;
         P = P * cs.y;
 #pragma unroll
@@ -259,7 +325,7 @@ __device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &
     if (__builtin_amdgcn_ballot_w64(lg > st.m + 8.f) != 0ull) {
         const float pm = head_reduce<G, true>(lg);
         const float mn = fmaxf(st.m, pm);
-        const float alpha = exp2f(st.m - mn);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
         st.l *= alpha;
         float sc[4];
 #pragma unroll
@@ -270,7 +336,7 @@ __device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &
         }
         st.m = mn;
     }
-    const float pe = exp2f(lg - st.m);
+    const float pe = __builtin_amdgcn_exp2f(lg - st.m);
     st.l += (j < G) ? pe : 0.f;   // for G < 4 several lanes carry the same head: count it once
 
     // ---- P (G x 16) to the MFMA A layout, split hi + lo in bf16 ----
@@ -361,8 +427,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ __attribute__((aligned(16))) float pbuf[kWaves][G * 16];
     __shared__ float mo[kWaves][2 * G][D];
     __shared__ float mml[kWaves][G][2];
-    // query halves of every tier present (mixed-tier pools only)
-    __shared__ __attribute__((aligned(16))) uint32_t uq_lds[TB == 0 ? 5 * D * G / 2 : 4];
+    // query preparation: the G query rows, their suffix sums, the edge tables
+    // of the tiers present, and the resulting packed unit directions
+    __shared__ float qs[G][D];
+    __shared__ double qT[G][D];
+    __shared__ double c2s[kThrEntries], s2s[kThrEntries];
+    __shared__ __attribute__((aligned(16))) _Float16 uq_lds[(TB == 0 ? 5 : 1) * D * G];
+    __shared__ float sq_lds[G];
 
     if constexpr (TB != 0) {
         // only this tier's tables and the (1, 1) padding entries it can index
@@ -372,15 +443,105 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int e = tid; e < kLutEntries; e += kThreads) lut[e] = A.lut[e];
     }
     rlev[tid] = A.rlev[kvh * 256 + tid];
-    const uint32_t *uq_glb = reinterpret_cast<const uint32_t *>(A.uq + ((int64_t)seq * A.hkv + kvh) * A.nt * D * G);
-    if constexpr (TB == 0)
-        for (int e = tid; e < A.nt * D * G / 2; e += kThreads) uq_lds[e] = uq_glb[e];
-    __syncthreads();
-
+    for (int e = tid; e < G * D; e += kThreads) qs[e / D][e % D] = A.q[head0 * D + e];
+    // this wave's first block-table entries, requested before the query prep
+    const int64_t bt_row = (int64_t)seq * A.max_pages;
     const int ppw = A.pps / kWaves;
     const int wp0 = p0 + wave * ppw;
     const int wp1 = min(wp0 + ppw, p1);
-
+    const int ph_first = (wp0 + lane < wp1) ? A.block_table[bt_row + wp0 + lane] : -1;
+    for (int b = 2; b <= 8; ++b) {
+        if (!((A.tier_mask >> b) & 1u)) continue;
+        for (int e = tid; e < (1 << b); e += kThreads) {
+            c2s[thr_off(b) + e] = A.cos2[thr_off(b) + e];
+            s2s[thr_off(b) + e] = A.sin2[thr_off(b) + e];
+        }
+        for (int e = tid; e < (1 << (b - 1)); e += kThreads) {
+            c2s[thr_off(b - 1) + e] = A.cos2[thr_off(b - 1) + e];
+            s2s[thr_off(b - 1) + e] = A.sin2[thr_off(b - 1) + e];
+        }
+    }
+    __syncthreads();
+    // Query prep, section 2.1's c_q: suffix sums of each query row in the
+    // keys' backward order (one thread per head), then per tier the angle
+    // codes (bisection over the edge tables) and the decoded direction
+    // u_a = (prod_{k<a} sin c_k) * cos c_a as a product scan across a wave
+    // (one wave per head; fp32 is ample for a value stored as fp16).
+    if (tid < G) {
+        float x[D];   // the row in registers: the LDS reads leave the serial add chain
+#pragma unroll
+        for (int a = 0; a < D; ++a) x[a] = qs[tid][a];
+        double T = add_square(0.0, x[D - 1]);
+        qT[tid][D - 1] = T;
+#pragma unroll
+        for (int a = D - 2; a >= 0; --a) {
+            T = add_square(T, x[a]);
+            qT[tid][a] = T;
+        }
+        sq_lds[tid] = (float)((double)A.scale * sqrt(T) * 1.4426950408889634);
+    }
+    __syncthreads();
+    if (wave < G) {
+        const int h = wave;
+        constexpr int PL = D / 64;   // components per lane
+        const double qn = sqrt(qT[h][0]);
+        int ti = 0;
+        for (int b = 2; b <= 8; ++b) {
+            if (!((A.tier_mask >> b) & 1u)) continue;
+            float uv[PL];
+            if (A.query_mode == 1) {
+#pragma unroll
+                for (int r = 0; r < PL; ++r) {
+                    const int a = lane * PL + r;
+                    uv[r] = qn > 0.0 ? (float)((double)qs[h][a] / qn) : 0.f;
+                }
+            } else {
+                float cs[PL], sn[PL];
+#pragma unroll
+                for (int r = 0; r < PL; ++r) {
+                    const int a = lane * PL + r;
+                    cs[r] = 1.f;
+                    sn[r] = 1.f;
+                    if (a < D - 2) {
+                        const int c = polar_code((double)qs[h][a], qT[h][a + 1], b, c2s + thr_off(b), s2s + thr_off(b));
+                        const float2 e = lut[lut_polar(b) + c];
+                        cs[r] = e.x;
+                        sn[r] = e.y;
+                    } else if (a == D - 2) {
+                        const int c = azimuth_code((double)qs[h][D - 2], (double)qs[h][D - 1], b,
+                                                   c2s + thr_off(b - 1), s2s + thr_off(b - 1));
+                        const float2 e = lut[lut_azimuth(b) + c];
+                        cs[r] = e.x;
+                        sn[r] = e.y;
+                    }
+                }
+                float tot = 1.f;
+#pragma unroll
+                for (int r = 0; r < PL; ++r) tot *= sn[r];
+                float incl = tot;   // inclusive product scan of the lanes' sine products
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float v = __shfl_up(incl, off);
+                    if (lane >= off) incl *= v;
+                }
+                float P = __shfl_up(incl, 1);
+                if (lane == 0) P = 1.f;
+#pragma unroll
+                for (int r = 0; r < PL; ++r) {
+                    uv[r] = P * cs[r];   // the last component has cs = 1: the product of all d-1 sines
+                    P *= sn[r];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < PL; ++r) {
+                const int a = lane * PL + r;
+                const int sl = a / (D / 4), i = a % (D / 4);
+                uq_lds[((ti * 4 + sl) * (D / 4) + i) * G + h] = (_Float16)uv[r];
+            }
+            ++ti;
+        }
+    }
+    __syncthreads();
     WaveState st{-INFINITY, 0.f};
     v4f acc[NT];
 #pragma unroll
@@ -388,17 +549,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     uint32_t u[D * G / 8];
     int cur_b = -1;
     const int jq = lane & 3;
+    const uint32_t *uqw = reinterpret_cast<const uint32_t *>(uq_lds);
     if constexpr (TB != 0) {
-        load_query<D, G>(reinterpret_cast<const uint4 *>(uq_glb + (A.tslot[TB] * 4 + jq) * (D * G / 8)), u);
+        load_query<D, G>(reinterpret_cast<const uint4 *>(uqw + jq * (D * G / 8)), u);
         cur_b = TB;
     } else {
 #pragma unroll
         for (int i = 0; i < D * G / 8; ++i) u[i] = 0u;
     }
     // this lane's head in the softmax: j % G
-    const float sq = A.sq[head0 + ((lane & 3) % G)];
+    const float sq = sq_lds[(lane & 3) % G];
 
-    const int64_t bt_row = (int64_t)seq * A.max_pages;
     float *pb = pbuf[wave];
 
     for (int c0 = wp0; c0 < wp1; c0 += 64) {
@@ -409,7 +570,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         int e_pg = c0 + lane, e_phys = -1, e_bits = 0;
         uint32_t e_lo = 0, e_hi = 0;
         if (lane < cn) {
-            const int ph = A.block_table[bt_row + c0 + lane];
+            const int ph = (c0 == wp0) ? ph_first : A.block_table[bt_row + c0 + lane];
             const bool ok = ph >= 0 && (int64_t)ph < A.num_pages;
             const int bb = ok ? (int)A.page_bits[ph] : 0;
             const bool okb = ok && bb >= 2 && bb <= 8 && ((A.tier_mask >> bb) & 1u);
@@ -455,7 +616,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         auto ensure_query = [&](int b) {
             if constexpr (TB == 0) {
                 if (b != cur_b) {
-                    load_query<D, G>(reinterpret_cast<const uint4 *>(uq_lds + (A.tslot[b] * 4 + jq) * (D * G / 8)), u);
+                    load_query<D, G>(reinterpret_cast<const uint4 *>(uqw + (A.tslot[b] * 4 + jq) * (D * G / 8)), u);
                     cur_b = b;
                 }
             }
@@ -526,10 +687,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 // Split merge: one workgroup of d threads per (sequence, query head):
 // M = max_s m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  The
-// (m, l) pairs are wave-uniform (scalar loads); the o_s loads of a thread
-// are independent and unrolled.  A sequence with no resident token gets 0.
+// (m, l) pairs are read by one thread each and combined in LDS; every o_s
+// read of a thread is independent of the others.  A sequence with no
+// resident token gets 0.
 template <int D>
 __global__ __launch_bounds__(D) void k_merge(MergeArgs A) {
+    __shared__ float sm[D], sl[D];
+    __shared__ float red[D / 64];
     const int row = blockIdx.x;
     const int seq = row / A.hq;
     const int e = threadIdx.x;
@@ -539,16 +703,36 @@ __global__ __launch_bounds__(D) void k_merge(MergeArgs A) {
     const int ns = (npages + A.pps - 1) / A.pps;
     const float *ml = A.part_ml + (int64_t)row * A.nsplit * 2;
     const float *po = A.part_o + (int64_t)row * A.nsplit * D + e;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-        for (int s = 0; s < ns; ++s) {
-            const float sc = exp2f(ml[2 * s] - M);
-            L += sc * ml[2 * s + 1];
-            O += sc * po[(int64_t)s * D];
+    float O = 0.f, L = 0.f, M = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += D) {   // D splits per round (one round in practice)
+        const int n = min(D, ns - s0);
+        float m = -INFINITY;
+        if (e < n) {
+            m = ml[2 * (s0 + e)];
+            sm[e] = m;
+            sl[e] = ml[2 * (s0 + e) + 1];
         }
+        float v = m;
+        for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+        if ((e & 63) == 0) red[e >> 6] = v;
+        __syncthreads();
+        float Mr = red[0];
+#pragma unroll
+        for (int w = 1; w < D / 64; ++w) Mr = fmaxf(Mr, red[w]);
+        const float Mn = fmaxf(M, Mr);
+        if (Mn != -INFINITY) {
+            const float r = exp2f(M - Mn);
+            O *= r;
+            L *= r;
+#pragma unroll 8
+            for (int s = 0; s < n; ++s) {
+                const float sc = exp2f(sm[s] - Mn);
+                L += sc * sl[s];
+                O += sc * po[(int64_t)(s0 + s) * D];
+            }
+        }
+        M = Mn;
+        __syncthreads();
     }
     A.out[(int64_t)row * D + e] = (M != -INFINITY) ? O / L : 0.f;
 }

@@ -40,7 +40,7 @@ struct ska_cache {
     void *d_ws = nullptr;
     size_t ws_bytes = 0;
     // kernel timing (ska_profile_begin / ska_profile_read)
-    std::vector<hipEvent_t> prof_ev;  // 4 per recorded call
+    std::vector<hipEvent_t> prof_ev;  // 3 per recorded call
     int prof_max = 0, prof_n = 0;
 };
 
@@ -357,38 +357,17 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     const int nsplit = (max_pages + pps - 1) / pps;
     if ((int64_t)nsplit * hkv > (1ll << 31) || batch > 65535 || nsplit > (1 << 30)) return SKA_ERR_UNSUPPORTED;
 
-    // workspace: [query scales | query directions (fp16) | partial o | partial (m, l)]
-    const size_t sq_n = (size_t)batch * num_q_heads;
-    const size_t uq_n = (size_t)batch * hkv * c->nt * d * G;
+    // workspace: [partial o | partial (m, l)]
     const size_t po_n = (size_t)batch * num_q_heads * nsplit * d;
     const size_t pm_n = (size_t)batch * num_q_heads * nsplit * 2;
-    const size_t off_sq = 0;
-    const size_t off_uq = off_sq + align256(sq_n * 4);
-    const size_t off_po = off_uq + align256(uq_n * 2), off_pm = off_po + align256(po_n * 4);
+    const size_t off_po = 0, off_pm = off_po + align256(po_n * 4);
     hipStream_t s = (hipStream_t)stream;
     ska_status st = ensure_ws(c, off_pm + align256(pm_n * 4), s);
     if (st != SKA_OK) return st;
     char *ws = (char *)c->d_ws;
     hipEvent_t *ev = nullptr;
-    if (c->prof_n < c->prof_max) ev = &c->prof_ev[4 * (size_t)c->prof_n++];
+    if (c->prof_n < c->prof_max) ev = &c->prof_ev[3 * (size_t)c->prof_n++];
     if (ev && hipEventRecord(ev[0], s) != hipSuccess) return SKA_ERR_HIP;
-
-    QPrepArgs qa{};
-    qa.q = q;
-    qa.B = batch;
-    qa.hq = num_q_heads;
-    qa.hkv = hkv;
-    qa.d = d;
-    qa.G = G;
-    qa.tier_mask = c->pool.tier_mask;
-    qa.nt = c->nt;
-    qa.query_mode = c->pool.query_mode;
-    qa.scale = scale;
-    qa.tab = CodeTables{c->d_cos2, c->d_sin2, c->d_cen};
-    qa.uq = (_Float16 *)(ws + off_uq);
-    qa.sq = (float *)(ws + off_sq);
-    if (launch_qprep(qa, s) != hipSuccess) return SKA_ERR_HIP;
-    if (ev && hipEventRecord(ev[1], s) != hipSuccess) return SKA_ERR_HIP;
 
     DecodeArgs da{};
     da.kcode = c->pool.kcode;
@@ -398,8 +377,11 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     da.page_bits = c->pool.page_bits;
     da.block_table = block_table;
     da.seq_lens = seq_lens;
-    da.uq = (const _Float16 *)(ws + off_uq);
-    da.sq = (const float *)(ws + off_sq);
+    da.q = q;
+    da.cos2 = c->d_cos2;
+    da.sin2 = c->d_sin2;
+    da.scale = scale;
+    da.query_mode = c->pool.query_mode;
     da.lut = c->d_lut;
     da.rlev = c->d_rlev;
     da.part_o = (float *)(ws + off_po);
@@ -417,7 +399,7 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     da.nt = c->nt;
     for (int b = 0; b <= 8; ++b) da.tslot[b] = c->tslot[b];
     if (launch_decode(da, d, G, batch, s) != hipSuccess) return SKA_ERR_HIP;
-    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return SKA_ERR_HIP;
+    if (ev && hipEventRecord(ev[1], s) != hipSuccess) return SKA_ERR_HIP;
 
     MergeArgs ma{};
     ma.part_o = da.part_o;
@@ -430,7 +412,7 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     ma.pps = pps;
     ma.nsplit = nsplit;
     if (launch_merge(ma, batch, s) != hipSuccess) return SKA_ERR_HIP;
-    if (ev && hipEventRecord(ev[3], s) != hipSuccess) return SKA_ERR_HIP;
+    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return SKA_ERR_HIP;
 
     return SKA_OK;
 }
@@ -438,7 +420,7 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
 ska_status ska_profile_begin(ska_cache *c, int max_calls) {
     if (!c || max_calls < 0 || max_calls > (1 << 20)) return SKA_ERR_INVALID;
     prof_clear(c);
-    c->prof_ev.assign(4 * (size_t)max_calls, nullptr);
+    c->prof_ev.assign(3 * (size_t)max_calls, nullptr);
     for (auto &e : c->prof_ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             e = nullptr;
@@ -455,10 +437,10 @@ ska_status ska_profile_read(ska_cache *c, float *ms_out, int max_calls, int *n_o
     if (!c || !n_out || max_calls < 0 || (max_calls > 0 && !ms_out)) return SKA_ERR_INVALID;
     const int n = c->prof_n < max_calls ? c->prof_n : max_calls;
     for (int i = 0; i < n; ++i) {
-        hipEvent_t *ev = &c->prof_ev[4 * (size_t)i];
-        if (hipEventSynchronize(ev[3]) != hipSuccess) return SKA_ERR_HIP;
-        for (int k = 0; k < 3; ++k)
-            if (hipEventElapsedTime(&ms_out[3 * i + k], ev[k], ev[k + 1]) != hipSuccess) return SKA_ERR_HIP;
+        hipEvent_t *ev = &c->prof_ev[3 * (size_t)i];
+        if (hipEventSynchronize(ev[2]) != hipSuccess) return SKA_ERR_HIP;
+        for (int k = 0; k < 2; ++k)
+            if (hipEventElapsedTime(&ms_out[2 * i + k], ev[k], ev[k + 1]) != hipSuccess) return SKA_ERR_HIP;
     }
     *n_out = n;
     return SKA_OK;

@@ -58,17 +58,6 @@ struct EncodeArgs {
     uint32_t *err;
 };
 
-struct QPrepArgs {
-    const float *q;          // [B][hq][d]
-    int B, hq, hkv, d, G;
-    uint32_t tier_mask;
-    int nt;                  // tiers present in the mask
-    int query_mode;
-    float scale;             // softmax scale
-    CodeTables tab;
-    _Float16 *uq;            // [B][hkv][nt][4][d/4][G] unit query directions
-    float *sq;               // [B][hq] scale * |q| * log2(e)
-};
 
 struct DecodeArgs {
     const uint8_t *kcode;
@@ -78,8 +67,9 @@ struct DecodeArgs {
     const uint8_t *page_bits;
     const int32_t *block_table;
     const int32_t *seq_lens;
-    const _Float16 *uq;      // [B][hkv][nt][4][d/4][G]
-    const float *sq;         // [B][hq]
+    const float *q;          // [B][hq][d]
+    const double *cos2;      // [kThrEntries] edge tables (binary64)
+    const double *sin2;
     const float2 *lut;       // [kLutEntries]
     const float *rlev;       // [hkv][256] radius levels
     float *part_o;           // [B][hq][nsplit][d]
@@ -94,13 +84,14 @@ struct DecodeArgs {
     uint32_t tier_mask;
     int nt;
     int8_t tslot[9];         // tier b -> index among the tiers present
+    float scale;             // softmax scale
+    int query_mode;          // 0: coded query, 1: exact query direction
 };
 
 
 hipError_t launch_calibrate(const float *keys, int64_t n, int hkv, int d, unsigned long long *minmax,
                             hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
-hipError_t launch_qprep(const QPrepArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s);
 
 struct MergeArgs {
