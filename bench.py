@@ -71,9 +71,10 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w, nseq: int):
+def cpu_baseline(w, nseq: int, min_seconds: float):
     """The CPU oracle (plain fp64 C, all host threads) on the first `nseq`
-    sequences of the workload: encode untimed, decode timed."""
+    sequences of the workload: encode untimed, then the decode of those
+    sequences (all query heads) repeated until `min_seconds` have passed."""
     import numpy as np
     from long_context_decode_ada_amd import workloads as W
     from oracle import oracle as O
@@ -82,17 +83,21 @@ def cpu_baseline(w, nseq: int):
     rows = slice(0, int(w.seq_lens[:nseq].astype(np.int64).sum()))
     O.encode(pools, w.keys[rows], w.values[rows], w.slot[rows], w.radius_mode, rng)
     pairs = [(s, h) for s in range(nseq) for h in range(w.hq)]
-    t0 = time.perf_counter()
-    O.decode(pools, w.radius_mode, rng, w.q, w.block_table, w.seq_lens, pairs=pairs)
-    dt = time.perf_counter() - t0
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.decode(pools, w.radius_mode, rng, w.q, w.block_table, w.seq_lens, pairs=pairs)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= 100:
+            break
     ntok = int(w.seq_lens[:nseq].sum())
     per_tok = W.record_bytes(w.d, int(w.page_bits[w.block_table[0, 0]])) + 1 + 2 * w.d
     npg = sum((int(w.seq_lens[s]) + 15) // 16 for s in range(nseq))
-    nbytes = ntok * w.hkv * per_tok + npg * w.hkv * 5
+    nbytes = reps * (ntok * w.hkv * per_tok + npg * w.hkv * 5)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": O.max_threads(), "kind": "oracle",
-            "kv_tokens_per_s": ntok / dt, "seconds": dt,
-            "sample": "%d of %d sequences of %s (%d tokens, all %d query heads), decode only" %
-                      (nseq, w.B, w.name, ntok, w.hq)}
+            "kv_tokens_per_s": reps * ntok / dt, "seconds": dt,
+            "sample": "%d of %d sequences of %s (%d tokens, all %d query heads), decode only, %d passes" %
+                      (nseq, w.B, w.name, ntok, w.hq, reps)}
 
 
 def main():
@@ -103,7 +108,8 @@ def main():
     ap.add_argument("--workload", default="gqa_t32k")
     ap.add_argument("--copies", type=int, default=2, help="pool copies alternated across steps")
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle timing")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain copy kernel of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -188,7 +194,7 @@ def main():
     cpu = None
     if args.cpu_seqs > 0:
         log("timing the CPU oracle on %d sequences" % args.cpu_seqs)
-        cpu = cpu_baseline(w, min(args.cpu_seqs, w.B))
+        cpu = cpu_baseline(w, min(args.cpu_seqs, w.B), args.cpu_seconds)
         log("oracle: %.3f GB/s (%.1fs, %d threads)" % (cpu["value"], cpu["seconds"], cpu["cores"]))
 
     tiers = sorted({int(b) for b in np.unique(w.page_bits)})

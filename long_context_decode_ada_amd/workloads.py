@@ -28,6 +28,12 @@ Workloads (sizes at scale 1):
               {2,4,6,8} with p={.3,.4,.2,.1}; 1023 of the 2047 non-sink pages
               per sequence are evicted (absent from the block table);
               variable-size pages addressed through page_off
+
+Seeding: one root seed; each workload and role (lengths, pages, tiers,
+eviction, channel scales, query) has its own child stream, and keys and
+values are drawn in fixed chunks of 8192 tokens, each chunk from its own
+seed sequence, so a workload's bytes are the same whatever thread count
+draws them.
 """
 from __future__ import annotations
 
@@ -119,6 +125,30 @@ def _rope(x: np.ndarray, pos: np.ndarray, d: int) -> np.ndarray:
     out[..., :half] = x1 * c - x2 * s
     out[..., half:] = x2 * c + x1 * s
     return out
+
+
+CHUNK = 8192          # tokens per key/value random chunk
+
+
+def _fill_chunks(idx, n_tok, hkv, d, chan, pos_all, keys, values):
+    """Keys and values in fixed chunks of CHUNK tokens, chunk c drawn from
+    its own generator (seed sequence (SEED, workload, role, c)), so the
+    bytes do not depend on how many threads draw them."""
+    def one(c):
+        a, b = c * CHUNK, min((c + 1) * CHUNK, n_tok)
+        gk = np.random.default_rng(np.random.SeedSequence(SEED, spawn_key=(idx, 100, c)))
+        gv = np.random.default_rng(np.random.SeedSequence(SEED, spawn_key=(idx, 101, c)))
+        z = gk.standard_normal((b - a, hkv, d), dtype=np.float32)
+        keys[a:b] = z if chan is None else _rope(z * chan[None], pos_all[a:b], d)
+        values[a:b] = _bf16_bits(gv.standard_normal((b - a, hkv, d), dtype=np.float32))
+    nch = (n_tok + CHUNK - 1) // CHUNK
+    if nch <= 1:
+        for c in range(nch):
+            one(c)
+        return
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(8, nch)) as ex:
+        list(ex.map(one, range(nch)))
 
 
 def _streams(idx: int, n: int = 10):
@@ -217,27 +247,24 @@ def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool 
     n_tok = int(lens.astype(np.int64).sum())
     if not data:
         keys = np.zeros((0, hkv, d), np.float32)
+        values = np.zeros((0, hkv, d), np.uint16)
         q = np.zeros((B, hq, d), np.float32)
-    elif name == "tiny":
-        keys = r_keys.standard_normal((n_tok, hkv, d), dtype=np.float32)
-        q = r_q.standard_normal((B, hq, d), dtype=np.float32)
     else:
-        chan = r_scale.lognormal(0.0, 0.5, size=(hkv, d)).astype(np.float32)
+        plain = name == "tiny"
+        chan = None if plain else r_scale.lognormal(0.0, 0.5, size=(hkv, d)).astype(np.float32)
+        pos_all = np.concatenate(pos_list) if n_tok else np.zeros(0, np.int64)
         keys = np.empty((n_tok, hkv, d), np.float32)
+        values = np.empty((n_tok, hkv, d), np.uint16)
+        _fill_chunks(idx, n_tok, hkv, d, chan, pos_all, keys, values)
         q = np.empty((B, hq, d), np.float32)
-        o = 0
         for s in range(B):
             n = int(lens[s])
-            z = r_keys.standard_normal((n, hkv, d), dtype=np.float32)
-            keys[o: o + n] = _rope(z * chan[None], pos_list[s], d)
-            qpos = (int(pos_list[s][-1]) + 1) if n else 0
             qs = r_q.standard_normal((1, hq, d), dtype=np.float32)
-            q[s] = _rope(qs, np.array([qpos]), d)[0]
-            o += n
-    if data:
-        values = _bf16_bits(r_vals.standard_normal((n_tok, hkv, d), dtype=np.float32))
-    else:
-        values = np.zeros((0, hkv, d), np.uint16)
+            if plain:
+                q[s] = qs[0]
+            else:
+                qpos = (int(pos_list[s][-1]) + 1) if n else 0
+                q[s] = _rope(qs, np.array([qpos]), d)[0]
 
     slot = np.empty(n_tok, np.int64)
     o = 0
