@@ -45,6 +45,8 @@
 //  * Page pipeline: each wave orders its next 64 pages (valid first, by tier)
 //    in registers, then keeps the loads of page k+1 in flight (a second
 //    register set) while page k is computed.
+#include <type_traits>
+
 #include "ska_codes.h"
 #include "ska_internal.h"
 
@@ -54,6 +56,17 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994531f;
+
+// Pipeline depth and occupancy: two waves per SIMD, each keeping the loads
+// of the next page in flight while it computes one (kBufs register sets).
+#ifndef SKA_BUFS
+#define SKA_BUFS 2
+#endif
+#ifndef SKA_WAVES_PER_SIMD
+#define SKA_WAVES_PER_SIMD 2
+#endif
+constexpr int kBufs = SKA_BUFS;
+constexpr int kWavesPerSimd = SKA_WAVES_PER_SIMD;
 
 // DPP quad permutations (within groups of 4 lanes).
 template <int CTRL>
@@ -66,6 +79,48 @@ constexpr int kQuadXor1 = 0xB1;
 constexpr int kQuadXor2 = 0x4E;
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
+
+// x from the lane DPP control CTRL names, or 1 where there is no such lane
+// (or the row is outside ROWS)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+
+// binary64 lane operations, one 32-bit half at a time
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_or_zero_d(double x) {
+    const int64_t v = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, ROWS, 0xF, false);
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double bpermute_d(int src_lane, double x) {
+    const int64_t v = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)(uint32_t)v);
+    const int hi = __builtin_amdgcn_ds_bpermute(src_lane * 4, (int)(v >> 32));
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+    const int64_t v = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+// sum of x over the lanes above this one (binary64; a scan over the
+// reversed lanes: row shifts, row broadcasts, one lane shift)
+__device__ __forceinline__ double wave_suffix_sum_excl(double x) {
+    const int lane = threadIdx.x & 63;
+    double v = bpermute_d(63 - lane, x);
+    v += dpp_or_zero_d<0x111, 0xF>(v);   // row_shr:1
+    v += dpp_or_zero_d<0x112, 0xF>(v);   // row_shr:2
+    v += dpp_or_zero_d<0x114, 0xF>(v);   // row_shr:4
+    v += dpp_or_zero_d<0x118, 0xF>(v);   // row_shr:8
+    v += dpp_or_zero_d<0x142, 0xA>(v);   // row_bcast:15
+    v += dpp_or_zero_d<0x143, 0xC>(v);   // row_bcast:31
+    v = dpp_or_zero_d<0x138, 0xF>(v);    // wave_shr:1: exclusive
+    return bpermute_d(63 - lane, v);
+}
 
 template <int CTRL>
 __device__ __forceinline__ float rowperm(float x) {
@@ -171,6 +226,7 @@ template <int D>
 struct PageBuf {
     uint32_t cw[8];
     uint32_t rc;
+    uint32_t hb;   // the page header (its angle bit width), single-tier kernels
     uint2 vf[D / 16];
 };
 
@@ -178,6 +234,7 @@ struct PageBuf {
 struct PageDesc {
     int phys, b, p;
     uint64_t off;   // byte offset of the physical page's code block
+    bool live;      // false: the loads go through empty descriptors and read nothing
 };
 
 // Raw buffer descriptor (V#) over `bytes` bytes at a wave-uniform address:
@@ -189,7 +246,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int
 // Loads of one page: the page's code block, radius bytes and V block each
 // get a descriptor built in scalar registers; the per-lane offsets inside a
 // block are the same for every page.
-template <int D, int B>
+template <int D, int B, bool HDR>
 __device__ __forceinline__ void load_page_b(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
     constexpr int KB = record_bytes(D, B);
     constexpr int SW = KB / 16;
@@ -197,9 +254,10 @@ __device__ __forceinline__ void load_page_b(const DecodeArgs &A, const PageDesc 
     const int t = lane >> 2, j = lane & 3;
     const int q4 = lane >> 4, n16 = lane & 15;
     const int64_t pk = (int64_t)pd.phys * A.hkv + kvh;
-    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + pd.off + (uint64_t)kvh * kPage * KB, kPage * KB);
-    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(A.v + pk * (int64_t)D * kPage, D * kPage * 2);
-    const __amdgpu_buffer_rsrc_t rr = buf_rsrc(A.rcode + pk * kPage, kPage);
+    const int lv = __builtin_amdgcn_readfirstlane(pd.live ? 1 : 0);   // scalar: descriptors stay uniform
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + pd.off + (uint64_t)kvh * kPage * KB, lv * kPage * KB);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(A.v + pk * (int64_t)D * kPage, lv * D * kPage * 2);
+    const __amdgpu_buffer_rsrc_t rr = buf_rsrc(A.rcode + pk * kPage, lv * kPage);
     const int vo = t * KB + j * (KB / 4);
     if constexpr (SW == 1) {
         r.cw[0] = __builtin_amdgcn_raw_buffer_load_b32(rk, vo, 0, 0);
@@ -221,6 +279,11 @@ __device__ __forceinline__ void load_page_b(const DecodeArgs &A, const PageDesc 
         }
     }
     r.rc = __builtin_amdgcn_raw_buffer_load_b8(rr, t, 0, 0);
+    if constexpr (HDR) {
+        // the header travels with the page's data, so checking it waits for nothing else
+        const __amdgpu_buffer_rsrc_t rh = buf_rsrc(A.page_bits + pd.phys, lv);
+        r.hb = __builtin_amdgcn_raw_buffer_load_b8(rh, 0, 0, 0);
+    }
     const int vv = (n16 * kPage + 4 * q4) * 2;
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) {
@@ -232,14 +295,14 @@ __device__ __forceinline__ void load_page_b(const DecodeArgs &A, const PageDesc 
 template <int D, int TB>
 __device__ __forceinline__ void load_page(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
     if constexpr (TB != 0) {
-        load_page_b<D, TB>(A, pd, kvh, r);
+        load_page_b<D, TB, true>(A, pd, kvh, r);
     } else {
         switch (pd.b) {
-            case 2: load_page_b<D, 2>(A, pd, kvh, r); break;
-            case 3: load_page_b<D, 3>(A, pd, kvh, r); break;
-            case 4: load_page_b<D, 4>(A, pd, kvh, r); break;
-            case 6: load_page_b<D, 6>(A, pd, kvh, r); break;
-            default: load_page_b<D, 8>(A, pd, kvh, r); break;
+            case 2: load_page_b<D, 2, false>(A, pd, kvh, r); break;
+            case 3: load_page_b<D, 3, false>(A, pd, kvh, r); break;
+            case 4: load_page_b<D, 4, false>(A, pd, kvh, r); break;
+            case 6: load_page_b<D, 6, false>(A, pd, kvh, r); break;
+            default: load_page_b<D, 8, false>(A, pd, kvh, r); break;
         }
     }
 }
@@ -380,6 +443,11 @@ __device__ __forceinline__ void compute_page(const DecodeArgs &A, const PageDesc
     const int ntok = min(kPage, len - pd.p * kPage);
     const int64_t lbase = head0 * A.max_pages * kPage + (int64_t)pd.p * kPage;
     if constexpr (TB != 0) {
+        // a page whose header disagrees with the kernel's tier is flagged and skipped
+        if (__builtin_amdgcn_readfirstlane(r.hb) != TB) {
+            if ((threadIdx.x & 63) == 0) atomicOr(A.err, 4u);
+            return;
+        }
         compute_page_b<D, G, TB, DBG>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc);
     } else {
         switch (pd.b) {
@@ -407,13 +475,17 @@ __device__ __forceinline__ void load_query(const uint4 *src, uint32_t (&u)[D * G
 // TB: the angle bit width of every page when the pool has a single tier, or 0
 // (pages of mixed tiers, dispatched per page on the header).
 template <int D, int G, int TB, bool DBG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_decode(DecodeArgs A) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_decode(DecodeArgs A) {
     constexpr int NA = D / 4;
     constexpr int NT = D / 16;
     const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps per-wave values scalar
     const int q4 = lane >> 4, n16 = lane & 15;
     const int64_t head0 = (int64_t)seq * A.hq + (int64_t)kvh * G;
+    // The prologue is a short dependent chain; at raised priority it is not
+    // starved by the page loops of the other workgroup sharing the CU.
+    __builtin_amdgcn_s_setprio(2);
 
     int len = A.seq_lens[seq];
     len = max(0, min(len, A.max_pages * kPage));
@@ -435,97 +507,295 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ __attribute__((aligned(16))) _Float16 uq_lds[(TB == 0 ? 5 : 1) * D * G];
     __shared__ float sq_lds[G];
 
-    if constexpr (TB != 0) {
-        // only this tier's tables and the (1, 1) padding entries it can index
-        for (int e = tid; e < 2 << TB; e += kThreads) lut[lut_polar(TB) + e] = A.lut[lut_polar(TB) + e];
-        for (int e = tid; e < 1 << TB; e += kThreads) lut[kLutOnes + e] = A.lut[kLutOnes + e];
-    } else {
-        for (int e = tid; e < kLutEntries; e += kThreads) lut[e] = A.lut[e];
-    }
-    rlev[tid] = A.rlev[kvh * 256 + tid];
-    for (int e = tid; e < G * D; e += kThreads) qs[e / D][e % D] = A.q[head0 * D + e];
-    // this wave's first block-table entries, requested before the query prep
+    // ---- prologue.  Every global read it needs is issued at once, and the
+    // loads of the wave's first two pages go out before the query
+    // preparation, so that the preparation runs under their latency. ----
     const int64_t bt_row = (int64_t)seq * A.max_pages;
-    const int ppw = A.pps / kWaves;
-    const int wp0 = p0 + wave * ppw;
-    const int wp1 = min(wp0 + ppw, p1);
-    const int ph_first = (wp0 + lane < wp1) ? A.block_table[bt_row + wp0 + lane] : -1;
-    for (int b = 2; b <= 8; ++b) {
-        if (!((A.tier_mask >> b) & 1u)) continue;
-        for (int e = tid; e < (1 << b); e += kThreads) {
-            c2s[thr_off(b) + e] = A.cos2[thr_off(b) + e];
-            s2s[thr_off(b) + e] = A.sin2[thr_off(b) + e];
+    // this wave's run of the split: the first wave on each SIMD (waves
+    // 0..kWaves/2-1) takes ppw_first pages, the second waves share the rest
+    constexpr int kHalf = kWaves / 2;
+    int wofs, wcnt;
+    if (wave < kHalf) {
+        wofs = wave * A.ppw_first;
+        wcnt = A.ppw_first;
+    } else {
+        const int rest = A.pps - kHalf * A.ppw_first;
+        const int per = (rest + kHalf - 1) / kHalf;
+        wofs = kHalf * A.ppw_first + (wave - kHalf) * per;
+        wcnt = max(0, min(per, rest - (wave - kHalf) * per));
+    }
+    const int wp0 = min(p0 + wofs, p1);
+    const int wp1 = min(wp0 + wcnt, p1);
+    // block-table entries of a chunk: one clamped, unconditional load per lane
+    auto bt_raw = [&](int c0) { return A.block_table[bt_row + min(c0 + lane, A.max_pages - 1)]; };
+    auto bt_fetch = [&](int c0) {
+        const int v = bt_raw(c0);
+        return (c0 + lane < wp1) ? v : -1;
+    };
+    const int ph_first = bt_fetch(wp0);
+    static_assert(kBufs >= 2, "at least one page in flight");
+    // Tables and query rows to LDS: all loads first (clamped indices, no
+    // branches), then the stores, so the staging costs one memory round trip.
+    constexpr int kNL = (kLutEntries + kThreads - 1) / kThreads;
+    constexpr int kNT = (kThrEntries + kThreads - 1) / kThreads;
+    constexpr int kNQ = (G * D + kThreads - 1) / kThreads;
+    float2 st_lut[kNL];
+    double st_c2[kNT], st_s2[kNT];
+    float st_q[kNQ];
+#pragma unroll
+    for (int i = 0; i < kNL; ++i) st_lut[i] = A.lut[min(tid + i * kThreads, kLutEntries - 1)];
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) {
+        const int e = min(tid + i * kThreads, kThrEntries - 1);
+        st_c2[i] = A.cos2[e];
+        st_s2[i] = A.sin2[e];
+    }
+#pragma unroll
+    for (int i = 0; i < kNQ; ++i) st_q[i] = A.q[head0 * D + min(tid + i * kThreads, G * D - 1)];
+    const float st_r = A.rlev[kvh * 256 + (tid & 255)];
+    // (the stores use the same clamped indices: a thread past the end writes
+    // the last element's own value again, so every load is consumed on every
+    // path and the compiler's wait counts stay exact)
+#pragma unroll
+    for (int i = 0; i < kNL; ++i) lut[min(tid + i * kThreads, kLutEntries - 1)] = st_lut[i];
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) {
+        const int e = min(tid + i * kThreads, kThrEntries - 1);
+        c2s[e] = st_c2[i];
+        s2s[e] = st_s2[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kNQ; ++i) {
+        const int e = min(tid + i * kThreads, G * D - 1);
+        qs[e / D][e % D] = st_q[i];
+    }
+    rlev[tid & 255] = st_r;
+
+    // The wave's page list, 64 pages at a time, one page per lane: valid
+    // pages first (ordered by tier when tiers are mixed, so that the query
+    // registers change at most once per tier).  With a single tier the
+    // addresses follow from the block table alone; each page header is then
+    // read with the page's data and checked before the page is used.
+    int e_pg = 0, e_phys = -1, e_bits = 0, nvalid = 0;
+    uint32_t e_lo = 0, e_hi = 0;
+    auto page_list = [&](int c0, int ph) {
+        const int cn = min(64, wp1 - c0);
+        e_pg = c0 + lane;
+        e_phys = -1;
+        e_bits = 0;
+        e_lo = e_hi = 0;
+        int key = 15;
+        const bool inr = lane < cn;
+        const bool ok = inr && ph >= 0 && (int64_t)ph < A.num_pages;
+        if (inr && !ok) atomicOr(A.err, 2u);
+        if constexpr (TB != 0) {
+            e_phys = ok ? ph : -1;
+            key = ok ? TB : 15;
+        } else {
+            // header and offset of the page, read at a clamped (valid) id
+            const int phc = ok ? ph : 0;
+            const int bb = (int)A.page_bits[phc];
+            const uint64_t off = A.page_off ? A.page_off[phc] : (uint64_t)phc * (uint64_t)A.page_stride;
+            const bool okb = ok && bb >= 2 && bb <= 8 && ((A.tier_mask >> bb) & 1u);
+            if (ok && !okb) atomicOr(A.err, 4u);
+            e_phys = okb ? ph : -1;
+            e_bits = okb ? bb : 0;
+            key = okb ? bb : 15;
+            e_lo = okb ? (uint32_t)off : 0u;
+            e_hi = okb ? (uint32_t)(off >> 32) : 0u;
         }
-        for (int e = tid; e < (1 << (b - 1)); e += kThreads) {
-            c2s[thr_off(b - 1) + e] = A.cos2[thr_off(b - 1) + e];
-            s2s[thr_off(b - 1) + e] = A.sin2[thr_off(b - 1) + e];
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int rank = 0;
+        nvalid = 0;
+        constexpr int kKeys[6] = {2, 3, 4, 6, 8, 15};
+#pragma unroll
+        for (int vi = 0; vi < 6; ++vi) {
+            const int v = kKeys[vi];
+            if (TB != 0 && v != TB && v != 15) continue;
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(key == v);
+            if (v < key) rank += __popcll(bal);
+            else if (v == key) rank += __popcll(bal & lt);
+            if (v != 15) nvalid += __popcll(bal);
+        }
+        e_pg = __builtin_amdgcn_ds_permute(rank * 4, e_pg);
+        e_phys = __builtin_amdgcn_ds_permute(rank * 4, e_phys);
+        if constexpr (TB == 0) {
+            e_bits = __builtin_amdgcn_ds_permute(rank * 4, e_bits);
+            e_lo = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)e_lo);
+            e_hi = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)e_hi);
+        }
+    };
+    auto desc = [&](int k) {
+        PageDesc pd;
+        pd.phys = __builtin_amdgcn_readlane(e_phys, k);
+        pd.b = TB != 0 ? TB : __builtin_amdgcn_readlane(e_bits, k);
+        pd.p = __builtin_amdgcn_readlane(e_pg, k);
+        pd.live = true;
+        if constexpr (TB != 0) {
+            pd.off = (uint64_t)(uint32_t)pd.phys * (uint64_t)A.page_stride;
+        } else {
+            pd.off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)e_hi, k) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)e_lo, k);
+        }
+        return pd;
+    };
+    // kBufs register sets: the loads of pages k+1 .. k+kBufs-1 are in flight
+    // while page k is computed.  Loads are issued unconditionally (past the
+    // end they repeat the last page) so that the wait before each compute
+    // only covers the loads of the page being computed.
+    PageBuf<D> R[kBufs];
+    PageDesc dd[kBufs];
+    auto start_chunk = [&](int c0, int ph) {
+        page_list(c0, ph);
+        // issued even when the chunk has no valid page (then through empty
+        // descriptors that read nothing), so every path issues the same loads
+#pragma unroll
+        for (int i = 0; i < kBufs; ++i) {
+            dd[i] = desc(max(0, min(i, nvalid - 1)));
+            dd[i].live = nvalid > 0;
+            load_page<D, TB>(A, dd[i], kvh, R[i]);
+        }
+    };
+    // (pools of mixed tiers start after the preparation: their larger
+    // kernel has no registers to spare for two pages during it)
+    // Single tier: the wave walks its pages in order, reading the block
+    // table 64 entries (one per lane) at a time into two rotating register
+    // slots, the next slot always requested a chunk ahead; the page loads
+    // run kBufs pages ahead of the computation without a break at chunk
+    // boundaries.  Pages whose id is out of range are flagged and skipped.
+    const int nw = wp1 - wp0;
+    int e_ph0 = ph_first, e_ph1 = 0;
+    // descriptor of page k of the run, its id read from slot S (the caller
+    // knows which slot holds k's chunk; reading only that slot keeps the
+    // other one free to be refilled while its loads are in flight)
+    auto rdesc = [&](int k, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        PageDesc pd;
+        const int kc = max(0, min(k, nw - 1));
+        const int ph = __builtin_amdgcn_readlane(S ? e_ph1 : e_ph0, kc & 63);
+        const bool ok = ph >= 0 && (int64_t)ph < A.num_pages;
+        pd.live = ok && k < nw;
+        pd.phys = ok ? ph : 0;
+        pd.b = TB != 0 ? TB : 8;
+        pd.p = wp0 + kc;
+        pd.off = (uint64_t)(uint32_t)pd.phys * (uint64_t)A.page_stride;
+        if (!ok && k < nw && lane == 0) atomicOr(A.err, 2u);
+        return pd;
+    };
+    if constexpr (TB != 0) {
+        e_ph1 = bt_raw(wp0 + 64);
+#pragma unroll
+        for (int i = 0; i < kBufs; ++i) {
+            dd[i] = rdesc(i, std::integral_constant<int, 0>{});
+            load_page<D, TB>(A, dd[i], kvh, R[i]);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    // Query prep, section 2.1's c_q: suffix sums of each query row in the
-    // keys' backward order (one thread per head), then per tier the angle
-    // codes (bisection over the edge tables) and the decoded direction
-    // u_a = (prod_{k<a} sin c_k) * cos c_a as a product scan across a wave
-    // (one wave per head; fp32 is ample for a value stored as fp16).
-    if (tid < G) {
-        float x[D];   // the row in registers: the LDS reads leave the serial add chain
-#pragma unroll
-        for (int a = 0; a < D; ++a) x[a] = qs[tid][a];
-        double T = add_square(0.0, x[D - 1]);
-        qT[tid][D - 1] = T;
-#pragma unroll
-        for (int a = D - 2; a >= 0; --a) {
-            T = add_square(T, x[a]);
-            qT[tid][a] = T;
-        }
-        sq_lds[tid] = (float)((double)A.scale * sqrt(T) * 1.4426950408889634);
-    }
-    __syncthreads();
+
+    // Query prep, section 2.1's c_q: per tier, the angle codes of each query
+    // row and the decoded direction u_a = (prod_{k<a} sin c_k) * cos c_a
+    // (one wave per head, D/64 components per lane).  The suffix sums of
+    // squares the codes compare against are taken by a wave scan (fast, but
+    // in another order than the keys' backward sum); a code is accepted only
+    // when its decisions hold with a margin covering that reordering.  Any
+    // decision inside the margin sends the wave to the exact backward sum and
+    // the plain search, so the codes always equal the defining ones.
     if (wave < G) {
         const int h = wave;
-        constexpr int PL = D / 64;   // components per lane
-        const double qn = sqrt(qT[h][0]);
+        constexpr int PL = D / 64;   // components per lane: a = lane * PL + r
+        float xr[PL];
+#pragma unroll
+        for (int r = 0; r < PL; ++r) xr[r] = qs[h][lane * PL + r];
+        double loc = 0.0;
+#pragma unroll
+        for (int r = PL - 1; r >= 0; --r) loc = add_square(loc, xr[r]);
+        const double above = wave_suffix_sum_excl(loc);
+        double Sr[PL];   // S of component a = sum of x_k^2 over k > a
+        double t = above;
+#pragma unroll
+        for (int r = PL - 1; r >= 0; --r) {
+            Sr[r] = t;
+            t = add_square(t, xr[r]);
+        }
+        const double T0 = readlane_d(t, 0);   // |q|^2
+        const double qn = sqrt(T0);
+        if (lane == 0) sq_lds[h] = (float)((double)A.scale * qn * 1.4426950408889634);
+        const double xa = (double)qs[h][D - 2], ya = (double)qs[h][D - 1];   // the azimuth pair
+        const bool hp = (ya < 0.0) || (ya == 0.0 && xa < 0.0);
+        const double xpa = hp ? -xa : xa, ypa = hp ? -ya : ya;
         int ti = 0;
         for (int b = 2; b <= 8; ++b) {
             if (!((A.tier_mask >> b) & 1u)) continue;
             float uv[PL];
             if (A.query_mode == 1) {
 #pragma unroll
+                for (int r = 0; r < PL; ++r) uv[r] = qn > 0.0 ? (float)((double)xr[r] / qn) : 0.f;
+            } else {
+                // one code per component; polar and azimuth share the code path
+                int code[PL];
+                bool ok = true;
+#pragma unroll
                 for (int r = 0; r < PL; ++r) {
                     const int a = lane * PL + r;
-                    uv[r] = qn > 0.0 ? (float)((double)qs[h][a] / qn) : 0.f;
+                    const bool az = a == D - 2;
+                    const double x = az ? xpa : (double)xr[r];
+                    const double S = az ? ypa * ypa : Sr[r];
+                    const int bb = az ? b - 1 : b;
+                    bool okr;
+                    const int g = polar_code_checked(x, S, bb, c2s + thr_off(bb), s2s + thr_off(bb),
+                                                     polar_guess(x, S, bb), az ? 0.0 : 5e-14, okr);
+                    code[r] = g;
+                    ok = ok && (a >= D - 1 || okr);
                 }
-            } else {
+                if (__builtin_amdgcn_ballot_w64(!ok) != 0) {
+                    // rare: the exact backward suffix sums (one lane), then the plain search
+                    if (lane == 0) {
+                        double T = 0.0;
+                        for (int a2 = D - 1; a2 >= 0; --a2) {
+                            qT[h][a2] = T;   // sum over k > a2
+                            T = add_square(T, qs[h][a2]);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < PL; ++r) {
+                        const int a = lane * PL + r;
+                        if (a < D - 2) {
+                            const double x = (double)xr[r], S = qT[h][a];
+                            code[r] = polar_code_near(x, S, b, c2s + thr_off(b), s2s + thr_off(b), code[r]);
+                        } else if (a == D - 2) {
+                            code[r] = polar_code_near(xpa, ypa * ypa, b - 1, c2s + thr_off(b - 1), s2s + thr_off(b - 1),
+                                                      code[r]);
+                        }
+                    }
+                }
                 float cs[PL], sn[PL];
 #pragma unroll
                 for (int r = 0; r < PL; ++r) {
                     const int a = lane * PL + r;
                     cs[r] = 1.f;
                     sn[r] = 1.f;
-                    if (a < D - 2) {
-                        const int c = polar_code((double)qs[h][a], qT[h][a + 1], b, c2s + thr_off(b), s2s + thr_off(b));
-                        const float2 e = lut[lut_polar(b) + c];
-                        cs[r] = e.x;
-                        sn[r] = e.y;
-                    } else if (a == D - 2) {
-                        const int c = azimuth_code((double)qs[h][D - 2], (double)qs[h][D - 1], b,
-                                                   c2s + thr_off(b - 1), s2s + thr_off(b - 1));
-                        const float2 e = lut[lut_azimuth(b) + c];
-                        cs[r] = e.x;
-                        sn[r] = e.y;
+                    if (a < D - 1) {
+                        const int e = (a == D - 2) ? lut_azimuth(b) + (hp ? (1 << (b - 1)) : 0) + code[r]
+                                                   : lut_polar(b) + code[r];
+                        const float2 v = lut[e];
+                        cs[r] = v.x;
+                        sn[r] = v.y;
                     }
                 }
                 float tot = 1.f;
 #pragma unroll
                 for (int r = 0; r < PL; ++r) tot *= sn[r];
-                float incl = tot;   // inclusive product scan of the lanes' sine products
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float v = __shfl_up(incl, off);
-                    if (lane >= off) incl *= v;
-                }
-                float P = __shfl_up(incl, 1);
-                if (lane == 0) P = 1.f;
+                // exclusive product scan of the lanes' sine products (DPP:
+                // row shifts, then the row broadcasts of lanes 15 and 31)
+                float incl = tot;
+                incl *= dpp_or_one<0x111, 0xF>(incl);   // row_shr:1
+                incl *= dpp_or_one<0x112, 0xF>(incl);   // row_shr:2
+                incl *= dpp_or_one<0x114, 0xF>(incl);   // row_shr:4
+                incl *= dpp_or_one<0x118, 0xF>(incl);   // row_shr:8
+                incl *= dpp_or_one<0x142, 0xA>(incl);   // row_bcast:15
+                incl *= dpp_or_one<0x143, 0xC>(incl);   // row_bcast:31
+                float P = dpp_or_one<0x138, 0xF>(incl);  // wave_shr:1 (lane 0 gets 1)
 #pragma unroll
                 for (int r = 0; r < PL; ++r) {
                     uv[r] = P * cs[r];   // the last component has cs = 1: the product of all d-1 sines
@@ -542,6 +812,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     }
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
     WaveState st{-INFINITY, 0.f};
     v4f acc[NT];
 #pragma unroll
@@ -559,88 +830,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     // this lane's head in the softmax: j % G
     const float sq = sq_lds[(lane & 3) % G];
-
     float *pb = pbuf[wave];
 
-    for (int c0 = wp0; c0 < wp1; c0 += 64) {
-        const int cn = min(64, wp1 - c0);
-        // this chunk's page list, one page per lane, valid pages first
-        // (ordered by tier when tiers are mixed, so that the query registers
-        // change at most once per tier)
-        int e_pg = c0 + lane, e_phys = -1, e_bits = 0;
-        uint32_t e_lo = 0, e_hi = 0;
-        if (lane < cn) {
-            const int ph = (c0 == wp0) ? ph_first : A.block_table[bt_row + c0 + lane];
-            const bool ok = ph >= 0 && (int64_t)ph < A.num_pages;
-            const int bb = ok ? (int)A.page_bits[ph] : 0;
-            const bool okb = ok && bb >= 2 && bb <= 8 && ((A.tier_mask >> bb) & 1u);
-            if (!ok) atomicOr(A.err, 2u);
-            else if (!okb) atomicOr(A.err, 4u);
-            if (okb) {
-                e_phys = ph;
-                e_bits = bb;
-                const uint64_t off = A.page_off ? A.page_off[ph] : (uint64_t)ph * (uint64_t)A.page_stride;
-                e_lo = (uint32_t)off;
-                e_hi = (uint32_t)(off >> 32);
+    auto ensure_query = [&](int b) {
+        if constexpr (TB == 0) {
+            if (b != cur_b) {
+                load_query<D, G>(reinterpret_cast<const uint4 *>(uqw + (A.tslot[b] * 4 + jq) * (D * G / 8)), u);
+                cur_b = b;
             }
         }
-        const int key = (e_phys >= 0) ? e_bits : 15;
-        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        int rank = 0, nvalid = 0;
-        constexpr int kKeys[6] = {2, 3, 4, 6, 8, 15};
+    };
+    if constexpr (TB != 0) {
+        static_assert(64 % kBufs == 0, "pipeline depth divides the chunk");
+        // Pages [kc, kc + 64) take their ids from slot 0 and [kc + 64, kc + 128)
+        // from slot 1.  Within a half, the loads issued while its last kBufs
+        // pages are computed belong to the next chunk (the other slot); at
+        // that point this half's slot is refilled with the chunk after next.
+        auto step = [&](int k, auto cur, auto nxt, bool refill, int refill_c0) {
+            constexpr int SC = decltype(cur)::value;
 #pragma unroll
-        for (int vi = 0; vi < 6; ++vi) {
-            const int v = kKeys[vi];
-            if (TB != 0 && v != TB && v != 15) continue;
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(key == v);
-            if (v < key) rank += __popcll(bal);
-            else if (v == key) rank += __popcll(bal & lt);
-            if (v != 15) nvalid += __popcll(bal);
-        }
-        e_pg = __builtin_amdgcn_ds_permute(rank * 4, e_pg);
-        e_phys = __builtin_amdgcn_ds_permute(rank * 4, e_phys);
-        e_bits = __builtin_amdgcn_ds_permute(rank * 4, e_bits);
-        e_lo = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)e_lo);
-        e_hi = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)e_hi);
-        if (nvalid == 0) continue;
-
-        auto desc = [&](int k) {
-            PageDesc pd;
-            pd.phys = __builtin_amdgcn_readlane(e_phys, k);
-            pd.b = TB != 0 ? TB : __builtin_amdgcn_readlane(e_bits, k);
-            pd.p = __builtin_amdgcn_readlane(e_pg, k);
-            pd.off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)e_hi, k) << 32) |
-                     (uint32_t)__builtin_amdgcn_readlane((int)e_lo, k);
-            return pd;
-        };
-        auto ensure_query = [&](int b) {
-            if constexpr (TB == 0) {
-                if (b != cur_b) {
-                    load_query<D, G>(reinterpret_cast<const uint4 *>(uqw + (A.tslot[b] * 4 + jq) * (D * G / 8)), u);
-                    cur_b = b;
+            for (int i = 0; i < kBufs; ++i) {
+                if (dd[i].live) compute_page<D, G, TB, DBG>(A, dd[i], R[i], len, head0, u, sq, lut, rlev, pb, st, acc);
+                if (refill && i == 0) {
+                    if (SC == 0) e_ph0 = bt_raw(refill_c0);
+                    else e_ph1 = bt_raw(refill_c0);
                 }
+                dd[i] = rdesc(k + i + kBufs, nxt);
+                load_page<D, TB>(A, dd[i], kvh, R[i]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
-        // two register sets: the loads of page k+1 are in flight while page k
-        // is computed.  The loads are issued unconditionally (past the end
-        // they repeat the last page) so that the wait before each compute
-        // only covers the loads of the page being computed.
-        PageBuf<D> R0, R1;
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        for (int kc = 0; kc < nw; kc += 128) {
+            // first half: slot 0
+            int k = kc;
+            for (; k + kBufs < kc + 64 && k < nw; k += kBufs) step(k, S0{}, S0{}, false, 0);
+            if (k < nw) step(k, S0{}, S1{}, true, wp0 + kc + 128);
+            k = kc + 64;
+            if (k >= nw) break;
+            // second half: slot 1
+            for (; k + kBufs < kc + 128 && k < nw; k += kBufs) step(k, S1{}, S1{}, false, 0);
+            if (k < nw) step(k, S1{}, S0{}, true, wp0 + kc + 192);
+        }
+    }
+    int ph_next = -1;   // the next chunk's block-table entries, requested a chunk ahead
+    for (int c0 = wp0; TB == 0 && c0 < wp1; c0 += 64) {
+        if (c0 != wp0) start_chunk(c0, ph_next);
+        else if (TB == 0) start_chunk(c0, ph_first);
+        ph_next = bt_fetch(c0 + 64);   // (all -1 past the wave's run)
+        if (nvalid == 0) continue;
         const int last = nvalid - 1;
-        PageDesc d0 = desc(0);
-        load_page<D, TB>(A, d0, kvh, R0);
-        for (int k = 0; k < nvalid; k += 2) {
-            const PageDesc d1 = desc(min(k + 1, last));
-            load_page<D, TB>(A, d1, kvh, R1);
-            __builtin_amdgcn_sched_barrier(0);   // issue these loads before waiting on page k
-            ensure_query(d0.b);
-            compute_page<D, G, TB, DBG>(A, d0, R0, len, head0, u, sq, lut, rlev, pb, st, acc);
-            d0 = desc(min(k + 2, last));
-            load_page<D, TB>(A, d0, kvh, R0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (k + 1 < nvalid) {
-                ensure_query(d1.b);
-                compute_page<D, G, TB, DBG>(A, d1, R1, len, head0, u, sq, lut, rlev, pb, st, acc);
+        for (int k = 0; k < nvalid; k += kBufs) {
+#pragma unroll
+            for (int i = 0; i < kBufs; ++i) {
+                if (k + i < nvalid) {
+                    ensure_query(dd[i].b);
+                    compute_page<D, G, TB, DBG>(A, dd[i], R[i], len, head0, u, sq, lut, rlev, pb, st, acc);
+                }
+                dd[i] = desc(min(k + i + kBufs, last));
+                load_page<D, TB>(A, dd[i], kvh, R[i]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -757,7 +1007,8 @@ hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s
     if (B == 0) return hipSuccess;
     const dim3 grid((unsigned)a.nsplit, (unsigned)a.hkv, (unsigned)B);
     int tb = 0;
-    if (__builtin_popcount(a.tier_mask) == 1) tb = __builtin_ctz(a.tier_mask);
+    // single-tier pools at a fixed page stride take the tier-specialised kernel
+    if (__builtin_popcount(a.tier_mask) == 1 && !a.page_off) tb = __builtin_ctz(a.tier_mask);
     if (d == 128) {
         if (G == 4) launch_dg<128, 4>(a, tb, grid, s);
         else if (G == 2) launch_dg<128, 2>(a, tb, grid, s);

@@ -48,6 +48,24 @@ namespace {
 
 bool tiers_ok(uint32_t mask) { return mask != 0 && (mask & ~kSupportedTiers) == 0; }
 
+// A decode workgroup holds two waves on each SIMD of its CU.  Measured on
+// MI355X, the wave dispatched first to a SIMD is served memory requests
+// ahead of the second and streams pages about 1.17x as fast, so with equal
+// page counts the second waves finish last.  The first wave on each SIMD
+// therefore takes the larger share of a split: the shares stay fixed (the
+// result does not depend on timing) and both waves finish together.
+#ifndef SKA_FIRST_WAVE_RATE
+#define SKA_FIRST_WAVE_RATE 1.17
+#endif
+constexpr double kFirstWaveRate = SKA_FIRST_WAVE_RATE;
+
+int first_wave_pages(int pps) {
+    const int half = kWaves / 2;
+    int n = (int)(pps * kFirstWaveRate / (half * (1.0 + kFirstWaveRate)) + 0.5);
+    if (n * half > pps) n = pps / half;
+    return n;
+}
+
 int max_tier(uint32_t mask) {
     int b = 0;
     for (int i = 2; i <= 8; ++i)
@@ -349,7 +367,7 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
         pps = (max_pages + num_splits - 1) / num_splits;
     } else {
         const int64_t total = (int64_t)batch * hkv * max_pages;
-        const int64_t target = 4ll * c->num_cus;  // workgroups
+        const int64_t target = (int64_t)c->num_cus;  // workgroups: one per CU
         pps = (int)((total + target - 1) / target);
     }
     pps = ((pps + kWaves - 1) / kWaves) * kWaves;
@@ -394,6 +412,7 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     da.hq = num_q_heads;
     da.max_pages = max_pages;
     da.pps = pps;
+    da.ppw_first = first_wave_pages(pps);
     da.nsplit = nsplit;
     da.tier_mask = c->pool.tier_mask;
     da.nt = c->nt;

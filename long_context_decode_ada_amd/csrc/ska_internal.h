@@ -8,7 +8,10 @@
 namespace ska {
 
 constexpr int kPage = 16;
-constexpr int kWaves = 4;               // waves per decode workgroup
+#ifndef SKA_WAVES
+#define SKA_WAVES 8
+#endif
+constexpr int kWaves = SKA_WAVES;       // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 
 // Bytes of one key record: 16 * ceil((d-1) * b / 128).
@@ -80,6 +83,7 @@ struct DecodeArgs {
     int64_t page_stride;
     int hkv, hq, max_pages;
     int pps;                 // pages per split (multiple of kWaves)
+    int ppw_first;           // pages of each of the first kWaves/2 waves of a split
     int nsplit;
     uint32_t tier_mask;
     int nt;

@@ -71,7 +71,11 @@ def test_split_count_and_determinism():
         else:
             assert np.array_equal(g["logits"], base["logits"], equal_nan=True)
             assert np.array_equal(g["out"], g["out_dbg"]) or np.abs(g["out"] - g["out_dbg"]).max() < 1e-6
-            assert np.abs(g["out"] - base["out"]).max() < 1e-5
+            # P enters P.V as hi + lo bf16 (16 significant bits, relative
+            # error <= 2^-16), and a different split count rescales P against
+            # different running maxima, so outputs may move by up to about
+            # 2^-16 * max|v| (|v| <= ~5 here) between split counts
+            assert np.abs(g["out"] - base["out"]).max() < 1e-4
 
 
 def test_ragged_edges_zero_one_and_page_boundaries():
