@@ -124,3 +124,28 @@ def test_no_poison_read_from_unused_pages():
     w = W.make("ragged_b64", 1 / 64, batch=16)
     g = gpu_run(w, poison=True)
     assert np.isfinite(g["out"]).all()
+
+
+def test_queries_and_keys_on_bin_edges():
+    """Rows whose angles sit exactly on bin edges (pi/4 and 3pi/4 are edges at
+    every b >= 2; zero tails give zero sub-vectors): ties go to the upper bin
+    on both sides, and the query codes take the exact path, not the margin
+    test (their sums are exact, so the margin test cannot accept them)."""
+    for name, scale in (("gqa_t32k", 1 / 64), ("mixed_tiers", 1 / 32)):
+        w = W.make(name, scale, batch=2)
+        d = w.d
+        edge = [np.r_[1.0, 1.0, np.zeros(d - 2)], np.r_[-1.0, 1.0, np.zeros(d - 2)],
+                np.r_[np.zeros(d - 2), -1.0, 0.0], np.r_[1.0, 0.0, 1.0, np.zeros(d - 3)]]
+        q = w.q.copy()
+        for i, e in enumerate(edge):
+            q[:, (5 * i) % w.hq] = e.astype(np.float32)
+        keys = w.keys.copy()
+        for t in range(16):
+            keys[t, t % w.hkv] = (edge[t % len(edge)] * (1 + t)).astype(np.float32)
+        w.keys = keys
+        rng = O.calibrate(w.keys)
+        g = gpu_run(w, q=q)
+        o = oracle_run(w, rng, q=q)
+        for k in ("kcode", "rcode", "v"):
+            assert np.array_equal(g["pools"][k], o["pools"][k]), (name, k)
+        compare(w, g, o, rng, q=q, label="%s edges" % name)
