@@ -144,14 +144,15 @@ ska_status ska_get_radius_range(const ska_cache *cache, double *range_out);
  * Synchronises `stream`. */
 ska_status ska_device_errors(ska_cache *cache, void *stream, uint32_t *flags_out);
 
-/* Kernel timing for the measurement of section 3 of the page (HBM traffic
- * and kernel-realised throughput on the paged substrate) and section 4
- * ("kernel-realised efficiency"): ska_profile_begin makes the next
- * `max_calls` ska_decode_attention calls on this cache record HIP events on
- * their stream around each of their two kernels (the paged decode, which
- * also prepares the query codes, and the split merge); 0 stops recording.
- * ska_profile_read waits for the recorded events and writes ms_out[i*2 + k]
- * for call i and kernel k, *n_out = calls recorded (at most max_calls). */
+/* Kernel timing, for measuring the decode kernel's achieved HBM throughput
+ * on the paged store (sections 1 and 4 of the page weigh the method by HBM
+ * traffic per generated token): ska_profile_begin makes the next `max_calls`
+ * ska_decode_attention calls on this cache record two HIP events on their
+ * stream, around the decode kernel (query preparation, paged decode and split
+ * merge); 0 stops recording.  The events skip the system-scope fence, so they
+ * barely perturb back-to-back calls.  ska_profile_read waits for the recorded
+ * events and writes ms_out[i] for call i, *n_out = calls recorded (at most
+ * max_calls). */
 ska_status ska_profile_begin(ska_cache *cache, int max_calls);
 ska_status ska_profile_read(ska_cache *cache, float *ms_out, int max_calls, int *n_out);
 

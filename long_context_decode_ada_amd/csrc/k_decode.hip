@@ -9,8 +9,11 @@
 //                streaming (the header is page_bits[phys]).
 // The pages describe no kernel.  This design is for CDNA4 (gfx950, wave64):
 //
-//  * Work: one workgroup of 4 waves per (sequence, kv head, split of pages);
-//    each wave walks a contiguous run of pages, one page per iteration.
+//  * Work: one workgroup of 8 waves (two per SIMD, one workgroup per CU)
+//    per (sequence, kv head, split of pages); each wave walks a contiguous
+//    run of the split's pages, one page per step.  The wave dispatched first
+//    to a SIMD is served memory ahead of the second, so the first four waves
+//    take a larger, fixed share of the split (set on the host).
 //  * f_b: a wave holds one page of one kv head: lane (t, j) = (token t of 16,
 //    slice j of 4).  Slice j covers components [j*d/4, (j+1)*d/4) of the
 //    direction.  In hyperspherical coordinates component a of u is
@@ -23,11 +26,11 @@
 //    f_h = sum_j C_j F_h,j with C_j = prod_{i<j} S_i.
 //  * The query side, the unit vector uq = u(centres(c_q)) per tier, is
 //    prepared in each workgroup's prologue (from the G query rows of its kv
-//    head: exact codes, then a product scan) as fp16 pairs and held packed in
-//    registers; v_fma_mix_f32 multiplies a half by the fp32 w and accumulates
-//    in fp32.  Rounding uq to fp16 moves f by at most 2^-11 (Cauchy-Schwarz
-//    over two unit vectors).  The logit is sq_h * r~ * f with
-//    sq_h = scale * |q_h| * log2(e) in fp32, so logits are in log2 units.
+//    head) as fp16 pairs and held packed in registers; v_fma_mix_f32
+//    multiplies a half by the fp32 w and accumulates in fp32.  Rounding uq to
+//    fp16 moves f by at most 2^-11 (Cauchy-Schwarz over two unit vectors).
+//    The logit is sq_h * r~ * f with sq_h = scale * |q_h| * log2(e) in fp32,
+//    so logits are in log2 units.
 //  * Softmax: online, per head, with the running max raised only when a logit
 //    exceeds it by more than 8 (a wave ballot); probabilities are bounded by
 //    2^8, which fp32 accumulation absorbs.
@@ -37,14 +40,19 @@
 //    lo in bf16 (rows 0..G-1 and G..2G-1 of the A operand), so the product
 //    keeps 16 mantissa bits of P; V enters as stored (bf16), dimension-major
 //    pages giving each lane its 4 consecutive tokens as one 8-byte load.
-//  * Split-T: each workgroup merges its 4 waves in LDS and writes one
-//    (m, l, o[d]) partial per query head; a second kernel (k_merge) combines
-//    the splits.  (Combining them in the last workgroup to finish, behind a
-//    device-scope fence, costs far more on this 8-XCD part: the fence writes
-//    back and invalidates the L2 of every workgroup's XCD.)
-//  * Page pipeline: each wave orders its next 64 pages (valid first, by tier)
-//    in registers, then keeps the loads of page k+1 in flight (a second
-//    register set) while page k is computed.
+//  * Page pipeline: the loads of page k+1 are in flight (a second register
+//    set) while page k is computed; loads are issued on every path (through
+//    empty descriptors past the end), so the compiler's wait counts stay
+//    exact and the pipeline never drains.  Single-tier pools read the block
+//    table 64 entries at a time into two rotating register slots; pools of
+//    mixed tiers order each 64-page chunk by tier (one query reload per tier).
+//  * Split-T: each workgroup merges its 8 waves in LDS and writes one
+//    (m, l, o[d]) partial per query head with device-coherent stores; the
+//    last workgroup of a (sequence, kv head) to finish (a device-scope
+//    counter) merges the splits with device-coherent loads.  No cache
+//    write-back or invalidation is involved: a device-scope fence, which
+//    writes back and invalidates a whole XCD's L2, measured about 6 us per
+//    launch on this part.
 #include <type_traits>
 
 #include "ska_codes.h"
@@ -491,7 +499,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     len = max(0, min(len, A.max_pages * kPage));
     const int npages = (len + kPage - 1) / kPage;
     const int p0 = split * A.pps;
-    if (p0 >= npages) return;  // whole workgroup, before any barrier
+    if (p0 >= npages) {   // whole workgroup, before any barrier
+        // a sequence with no resident token: its output rows are 0
+        if (npages == 0 && split == 0)
+            for (int e = threadIdx.x; e < G * D; e += kThreads) A.out[head0 * D + e] = 0.f;
+        return;
+    }
     const int p1 = min(p0 + A.pps, npages);
 
     __shared__ float2 lut[kLutEntries];
@@ -925,66 +938,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                 O += sc * (mo[w][h][e] + mo[w][G + h][e]);
             }
         }
+        // device-coherent stores (written through to memory): the merging
+        // workgroup, on any XCD, reads them with device-coherent loads
         const int64_t pi = (head0 + h) * A.nsplit + split;
-        A.part_o[pi * D + e] = O;
+        __hip_atomic_store(&A.part_o[pi * D + e], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (e == 0) {
-            A.part_ml[2 * pi + 0] = M;
-            A.part_ml[2 * pi + 1] = L;
+            __hip_atomic_store(&A.part_ml[2 * pi + 0], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&A.part_ml[2 * pi + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
-}
-
-// Split merge: one workgroup of d threads per (sequence, query head):
-// M = max_s m_s, out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.  The
-// (m, l) pairs are read by one thread each and combined in LDS; every o_s
-// read of a thread is independent of the others.  A sequence with no
-// resident token gets 0.
-template <int D>
-__global__ __launch_bounds__(D) void k_merge(MergeArgs A) {
-    __shared__ float sm[D], sl[D];
-    __shared__ float red[D / 64];
-    const int row = blockIdx.x;
-    const int seq = row / A.hq;
-    const int e = threadIdx.x;
-    int len = A.seq_lens[seq];
-    len = max(0, min(len, A.max_pages * kPage));
-    const int npages = (len + kPage - 1) / kPage;
-    const int ns = (npages + A.pps - 1) / A.pps;
-    const float *ml = A.part_ml + (int64_t)row * A.nsplit * 2;
-    const float *po = A.part_o + (int64_t)row * A.nsplit * D + e;
-    float O = 0.f, L = 0.f, M = -INFINITY;
-    for (int s0 = 0; s0 < ns; s0 += D) {   // D splits per round (one round in practice)
-        const int n = min(D, ns - s0);
-        float m = -INFINITY;
-        if (e < n) {
-            m = ml[2 * (s0 + e)];
-            sm[e] = m;
-            sl[e] = ml[2 * (s0 + e) + 1];
-        }
-        float v = m;
-        for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-        if ((e & 63) == 0) red[e >> 6] = v;
-        __syncthreads();
-        float Mr = red[0];
-#pragma unroll
-        for (int w = 1; w < D / 64; ++w) Mr = fmaxf(Mr, red[w]);
-        const float Mn = fmaxf(M, Mr);
-        if (Mn != -INFINITY) {
-            const float r = exp2f(M - Mn);
-            O *= r;
-            L *= r;
-#pragma unroll 8
-            for (int s = 0; s < n; ++s) {
-                const float sc = exp2f(sm[s] - Mn);
-                L += sc * sl[s];
-                O += sc * po[(int64_t)(s0 + s) * D];
+    // ---- merge of the splits by the last workgroup of this (sequence, KV
+    // head) to finish.  The partials above are device-coherent stores; once
+    // every wave has seen its stores complete (vmcnt(0): with device-scope
+    // stores that means visible to every XCD), one thread raises the group's
+    // counter.  The workgroup that raises it last reads the partials with
+    // device-coherent loads, merges them and clears
+    // the counter for the next call.  No cache write-back or invalidation is
+    // needed, since no plain store or load takes part. ----
+    __shared__ int s_last;
+    const int ns_g = (npages + A.pps - 1) / A.pps;   // workgroups that work on this group
+    const int group = seq * A.hkv + kvh;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&A.counters[group], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev + 1 == (unsigned)ns_g);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, e = idx % D;
+        const int64_t row = head0 + h;
+        float *ml = A.part_ml + row * A.nsplit * 2;
+        float *po = A.part_o + row * A.nsplit * D + e;
+        auto ld = [](float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+        float M = -INFINITY;
+        for (int sp = 0; sp < ns_g; ++sp) M = fmaxf(M, ld(ml + 2 * sp));
+        float O = 0.f, L = 0.f;
+        if (M != -INFINITY) {
+            for (int sp = 0; sp < ns_g; ++sp) {
+                const float sc = exp2f(ld(ml + 2 * sp) - M);
+                L += sc * ld(ml + 2 * sp + 1);
+                O += sc * ld(po + (int64_t)sp * D);
             }
         }
-        M = Mn;
-        __syncthreads();
+        A.out[row * D + e] = (M != -INFINITY) ? O / L : 0.f;
     }
-    A.out[(int64_t)row * D + e] = (M != -INFINITY) ? O / L : 0.f;
+    if (tid == 0) __hip_atomic_store(&A.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int G>
@@ -1021,11 +1022,14 @@ hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs &a, int B, hipStream_t s) {
-    if (B == 0) return hipSuccess;
-    const dim3 grid((unsigned)(B * a.hq));
-    if (a.d == 128) hipLaunchKernelGGL(k_merge<128>, grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL(k_merge<64>, grid, dim3(64), 0, s, a);
+__global__ void k_zero_u32(uint32_t *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

@@ -39,8 +39,10 @@ struct ska_cache {
     uint32_t *d_err = nullptr;
     void *d_ws = nullptr;
     size_t ws_bytes = 0;
+    uint32_t *d_cnt = nullptr;   // per (sequence, KV head) counters of the in-kernel merge
+    size_t cnt_n = 0;
     // kernel timing (ska_profile_begin / ska_profile_read)
-    std::vector<hipEvent_t> prof_ev;  // 3 per recorded call
+    std::vector<hipEvent_t> prof_ev;  // 2 per recorded call
     int prof_max = 0, prof_n = 0;
 };
 
@@ -177,6 +179,7 @@ void release(ska_cache *c) {
     hipFree(c->d_rlev);
     hipFree(c->d_err);
     hipFree(c->d_ws);
+    hipFree(c->d_cnt);
     delete c;
 }
 
@@ -254,6 +257,25 @@ ska_status calibrate(ska_cache *c, const float *keys, int64_t n, hipStream_t s) 
         range[2 * g + 1] = rhi;
     }
     return set_range(c, range.data());
+}
+
+// Counters of the in-kernel split merge: zero when allocated; each call
+// leaves them zero (the merging workgroup clears its group's counter).
+ska_status ensure_counters(ska_cache *c, size_t n, hipStream_t s) {
+    if (n <= c->cnt_n) return SKA_OK;
+    if (c->d_cnt) {
+        if (hipFree(c->d_cnt) != hipSuccess) return SKA_ERR_HIP;
+        c->d_cnt = nullptr;
+        c->cnt_n = 0;
+    }
+    const size_t want = n + n / 4 + 64;
+    if (hipMalloc(&c->d_cnt, want * sizeof(uint32_t)) != hipSuccess) {
+        c->d_cnt = nullptr;
+        return SKA_ERR_NOMEM;
+    }
+    if (launch_zero_u32(c->d_cnt, (int64_t)want, s) != hipSuccess) return SKA_ERR_HIP;
+    c->cnt_n = want;
+    return SKA_OK;
 }
 
 ska_status ensure_ws(ska_cache *c, size_t bytes, hipStream_t s) {
@@ -382,9 +404,10 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     hipStream_t s = (hipStream_t)stream;
     ska_status st = ensure_ws(c, off_pm + align256(pm_n * 4), s);
     if (st != SKA_OK) return st;
+    if ((st = ensure_counters(c, (size_t)batch * hkv, s)) != SKA_OK) return st;
     char *ws = (char *)c->d_ws;
     hipEvent_t *ev = nullptr;
-    if (c->prof_n < c->prof_max) ev = &c->prof_ev[3 * (size_t)c->prof_n++];
+    if (c->prof_n < c->prof_max) ev = &c->prof_ev[2 * (size_t)c->prof_n++];
     if (ev && hipEventRecord(ev[0], s) != hipSuccess) return SKA_ERR_HIP;
 
     DecodeArgs da{};
@@ -405,6 +428,8 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     da.part_o = (float *)(ws + off_po);
     da.part_ml = (float *)(ws + off_pm);
     da.logits = logits_dbg;
+    da.out = out;
+    da.counters = c->d_cnt;
     da.err = c->d_err;
     da.num_pages = c->pool.num_pages;
     da.page_stride = c->page_stride;
@@ -420,28 +445,15 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     if (launch_decode(da, d, G, batch, s) != hipSuccess) return SKA_ERR_HIP;
     if (ev && hipEventRecord(ev[1], s) != hipSuccess) return SKA_ERR_HIP;
 
-    MergeArgs ma{};
-    ma.part_o = da.part_o;
-    ma.part_ml = da.part_ml;
-    ma.seq_lens = seq_lens;
-    ma.out = out;
-    ma.hq = num_q_heads;
-    ma.d = d;
-    ma.max_pages = max_pages;
-    ma.pps = pps;
-    ma.nsplit = nsplit;
-    if (launch_merge(ma, batch, s) != hipSuccess) return SKA_ERR_HIP;
-    if (ev && hipEventRecord(ev[2], s) != hipSuccess) return SKA_ERR_HIP;
-
     return SKA_OK;
 }
 
 ska_status ska_profile_begin(ska_cache *c, int max_calls) {
     if (!c || max_calls < 0 || max_calls > (1 << 20)) return SKA_ERR_INVALID;
     prof_clear(c);
-    c->prof_ev.assign(3 * (size_t)max_calls, nullptr);
+    c->prof_ev.assign(2 * (size_t)max_calls, nullptr);
     for (auto &e : c->prof_ev) {
-        if (hipEventCreate(&e) != hipSuccess) {
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
             e = nullptr;
             prof_clear(c);
             return SKA_ERR_HIP;
@@ -456,10 +468,9 @@ ska_status ska_profile_read(ska_cache *c, float *ms_out, int max_calls, int *n_o
     if (!c || !n_out || max_calls < 0 || (max_calls > 0 && !ms_out)) return SKA_ERR_INVALID;
     const int n = c->prof_n < max_calls ? c->prof_n : max_calls;
     for (int i = 0; i < n; ++i) {
-        hipEvent_t *ev = &c->prof_ev[3 * (size_t)i];
-        if (hipEventSynchronize(ev[2]) != hipSuccess) return SKA_ERR_HIP;
-        for (int k = 0; k < 2; ++k)
-            if (hipEventElapsedTime(&ms_out[2 * i + k], ev[k], ev[k + 1]) != hipSuccess) return SKA_ERR_HIP;
+        hipEvent_t *ev = &c->prof_ev[2 * (size_t)i];
+        if (hipEventSynchronize(ev[1]) != hipSuccess) return SKA_ERR_HIP;
+        if (hipEventElapsedTime(&ms_out[i], ev[0], ev[1]) != hipSuccess) return SKA_ERR_HIP;
     }
     *n_out = n;
     return SKA_OK;

@@ -78,6 +78,8 @@ struct DecodeArgs {
     float *part_o;           // [B][hq][nsplit][d]
     float *part_ml;          // [B][hq][nsplit][2]
     float *logits;           // debug [B][hq][max_pages*16] or NULL
+    float *out;              // [B][hq][d]
+    uint32_t *counters;      // [B][hkv] finished workgroups per group, zero between calls
     uint32_t *err;
     int64_t num_pages;
     int64_t page_stride;
@@ -97,14 +99,7 @@ hipError_t launch_calibrate(const float *keys, int64_t n, int hkv, int d, unsign
                             hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
 
-struct MergeArgs {
-    const float *part_o;
-    const float *part_ml;
-    const int32_t *seq_lens;
-    float *out;
-    int hq, d, max_pages, pps, nsplit;
-};
-hipError_t launch_merge(const MergeArgs &a, int B, hipStream_t s);
 
 }  // namespace ska

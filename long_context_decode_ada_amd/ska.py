@@ -200,8 +200,8 @@ def profile_begin(cache: Cache, max_calls: int):
 
 
 def profile_read(cache: Cache, max_calls: int) -> np.ndarray:
-    """[calls][2] kernel milliseconds (decode incl. query prep, split merge)."""
-    ms = np.zeros((max(1, max_calls), 2), np.float32)
+    """[calls] decode-kernel milliseconds (query prep, paged decode, split merge)."""
+    ms = np.zeros(max(1, max_calls), np.float32)
     n = ctypes.c_int(0)
     _check(lib().ska_profile_read(cache.handle, ms.ctypes.data_as(ctypes.c_void_p), int(max_calls),
                                   ctypes.byref(n)), "ska_profile_read")
