@@ -486,7 +486,11 @@ template <int D, int G, int TB, bool DBG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_decode(DecodeArgs A) {
     constexpr int NA = D / 4;
     constexpr int NT = D / 16;
-    const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+    // split is the slowest grid dimension: the dispatcher hands out every
+    // group's first split before any second one, so the later splits of the
+    // long sequences of a ragged batch (and the empty workgroups past the end
+    // of the short ones) fill CUs as they free up
+    const int kvh = blockIdx.x, seq = blockIdx.y, split = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps per-wave values scalar
     const int q4 = lane >> 4, n16 = lane & 15;
@@ -524,17 +528,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // loads of the wave's first two pages go out before the query
     // preparation, so that the preparation runs under their latency. ----
     const int64_t bt_row = (int64_t)seq * A.max_pages;
-    // this wave's run of the split: the first wave on each SIMD (waves
-    // 0..kWaves/2-1) takes ppw_first pages, the second waves share the rest
+    // this wave's run of the split's p1 - p0 pages: the first wave on each
+    // SIMD (waves 0..kWaves/2-1) takes first_wave_pages of them, the second
+    // waves share the rest
     constexpr int kHalf = kWaves / 2;
+    const int fpw = first_wave_pages(p1 - p0);
     int wofs, wcnt;
     if (wave < kHalf) {
-        wofs = wave * A.ppw_first;
-        wcnt = A.ppw_first;
+        wofs = wave * fpw;
+        wcnt = fpw;
     } else {
-        const int rest = A.pps - kHalf * A.ppw_first;
+        const int rest = (p1 - p0) - kHalf * fpw;
         const int per = (rest + kHalf - 1) / kHalf;
-        wofs = kHalf * A.ppw_first + (wave - kHalf) * per;
+        wofs = kHalf * fpw + (wave - kHalf) * per;
         wcnt = max(0, min(per, rest - (wave - kHalf) * per));
     }
     const int wp0 = min(p0 + wofs, p1);
@@ -1006,7 +1012,7 @@ static void launch_dg(const DecodeArgs &a, int tb, dim3 grid, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s) {
     if (B == 0) return hipSuccess;
-    const dim3 grid((unsigned)a.nsplit, (unsigned)a.hkv, (unsigned)B);
+    const dim3 grid((unsigned)a.hkv, (unsigned)B, (unsigned)a.nsplit);
     int tb = 0;
     // single-tier pools at a fixed page stride take the tier-specialised kernel
     if (__builtin_popcount(a.tier_mask) == 1 && !a.page_off) tb = __builtin_ctz(a.tier_mask);

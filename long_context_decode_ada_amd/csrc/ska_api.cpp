@@ -13,6 +13,7 @@
 // library call and each product is rounded as written.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -49,24 +50,6 @@ struct ska_cache {
 namespace {
 
 bool tiers_ok(uint32_t mask) { return mask != 0 && (mask & ~kSupportedTiers) == 0; }
-
-// A decode workgroup holds two waves on each SIMD of its CU.  Measured on
-// MI355X, the wave dispatched first to a SIMD is served memory requests
-// ahead of the second and streams pages about 1.17x as fast, so with equal
-// page counts the second waves finish last.  The first wave on each SIMD
-// therefore takes the larger share of a split: the shares stay fixed (the
-// result does not depend on timing) and both waves finish together.
-#ifndef SKA_FIRST_WAVE_RATE
-#define SKA_FIRST_WAVE_RATE 1.17
-#endif
-constexpr double kFirstWaveRate = SKA_FIRST_WAVE_RATE;
-
-int first_wave_pages(int pps) {
-    const int half = kWaves / 2;
-    int n = (int)(pps * kFirstWaveRate / (half * (1.0 + kFirstWaveRate)) + 0.5);
-    if (n * half > pps) n = pps / half;
-    return n;
-}
 
 int max_tier(uint32_t mask) {
     int b = 0;
@@ -383,19 +366,29 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     if ((int64_t)batch * num_q_heads > (1ll << 30)) return SKA_ERR_UNSUPPORTED;
     if (scale == 0.f) scale = 1.0f / std::sqrt((float)d);
 
-    // split policy: pages per split (a multiple of the 4 waves)
+    // split policy: pages per split (a multiple of the waves).  Automatic:
+    // as if every sequence had max_pages pages, one workgroup per CU.  When
+    // the (sequence, KV head) groups alone already fill the CUs that gives
+    // one split, and in a ragged batch the longest sequences then run alone
+    // at the end; so there every sequence is cut into up to kTailSplits
+    // splits (of at least kMinSplitPages pages), which the dispatcher hands
+    // to CUs as they free up.
+    constexpr int kTailSplits = 4, kMinSplitPages = 64;
     int pps;
     if (num_splits > 0) {
         pps = (max_pages + num_splits - 1) / num_splits;
     } else {
         const int64_t total = (int64_t)batch * hkv * max_pages;
         const int64_t target = (int64_t)c->num_cus;  // workgroups: one per CU
-        pps = (int)((total + target - 1) / target);
+        pps = (int)std::min<int64_t>((total + target - 1) / target, max_pages);
+        if (pps >= max_pages) pps = std::max(kMinSplitPages, (max_pages + kTailSplits - 1) / kTailSplits);
     }
     pps = ((pps + kWaves - 1) / kWaves) * kWaves;
     if (pps < kWaves) pps = kWaves;
+    // the split index is the grid's z dimension (at most 65535)
+    if ((max_pages + pps - 1) / pps > 65535) pps = (((max_pages + 65534) / 65535 + kWaves - 1) / kWaves) * kWaves;
     const int nsplit = (max_pages + pps - 1) / pps;
-    if ((int64_t)nsplit * hkv > (1ll << 31) || batch > 65535 || nsplit > (1 << 30)) return SKA_ERR_UNSUPPORTED;
+    if (batch > 65535 || hkv > 65535) return SKA_ERR_UNSUPPORTED;
 
     // workspace: [partial o | partial (m, l)]
     const size_t po_n = (size_t)batch * num_q_heads * nsplit * d;
@@ -437,7 +430,6 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     da.hq = num_q_heads;
     da.max_pages = max_pages;
     da.pps = pps;
-    da.ppw_first = first_wave_pages(pps);
     da.nsplit = nsplit;
     da.tier_mask = c->pool.tier_mask;
     da.nt = c->nt;

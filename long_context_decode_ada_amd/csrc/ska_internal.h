@@ -14,6 +14,22 @@ constexpr int kPage = 16;
 constexpr int kWaves = SKA_WAVES;       // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 
+// A decode workgroup holds two waves on each SIMD of its CU.  Measured on
+// MI355X, the wave dispatched first to a SIMD is served memory requests
+// ahead of the second and streams pages about 1.17x as fast, so with equal
+// page counts the second waves finish last.  The first wave on each SIMD
+// therefore takes the larger share of a chunk of n pages: round(n r / (h (1 + r)))
+// pages with r the rate ratio and h = kWaves / 2.  The shares depend on n
+// only (not on timing), so results are reproducible.
+#ifndef SKA_FIRST_WAVE_RATE_PCT
+#define SKA_FIRST_WAVE_RATE_PCT 117
+#endif
+__host__ __device__ constexpr int first_wave_pages(int n) {
+    constexpr int h = kWaves / 2, r = SKA_FIRST_WAVE_RATE_PCT;
+    const int f = (2 * n * r + h * (100 + r)) / (2 * h * (100 + r));
+    return f * h > n ? n / h : f;
+}
+
 // Bytes of one key record: 16 * ceil((d-1) * b / 128).
 __host__ __device__ constexpr int record_bytes(int d, int b) { return 16 * (((d - 1) * b + 127) / 128); }
 
@@ -85,7 +101,6 @@ struct DecodeArgs {
     int64_t page_stride;
     int hkv, hq, max_pages;
     int pps;                 // pages per split (multiple of kWaves)
-    int ppw_first;           // pages of each of the first kWaves/2 waves of a split
     int nsplit;
     uint32_t tier_mask;
     int nt;
