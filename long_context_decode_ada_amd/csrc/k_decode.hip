@@ -499,18 +499,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // starved by the page loops of the other workgroup sharing the CU.
     __builtin_amdgcn_s_setprio(2);
 
-    int len = A.seq_lens[seq];
-    len = max(0, min(len, A.max_pages * kPage));
-    const int npages = (len + kPage - 1) / kPage;
-    const int p0 = split * A.pps;
-    if (p0 >= npages) {   // whole workgroup, before any barrier
-        // a sequence with no resident token: its output rows are 0
-        if (npages == 0 && split == 0)
-            for (int e = threadIdx.x; e < G * D; e += kThreads) A.out[head0 * D + e] = 0.f;
-        return;
-    }
-    const int p1 = min(p0 + A.pps, npages);
-
     __shared__ float2 lut[kLutEntries];
     __shared__ float rlev[256];
     __shared__ __attribute__((aligned(16))) float pbuf[kWaves][G * 16];
@@ -524,34 +512,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ __attribute__((aligned(16))) _Float16 uq_lds[(TB == 0 ? 5 : 1) * D * G];
     __shared__ float sq_lds[G];
 
-    // ---- prologue.  Every global read it needs is issued at once, and the
-    // loads of the wave's first two pages go out before the query
-    // preparation, so that the preparation runs under their latency. ----
+    // ---- prologue.  Every global read it needs is issued at once: the
+    // sequence length, the block-table entries of this wave's run (taken as
+    // if the split were full, which it is except for the last split of a
+    // sequence) and the tables; the loads of the wave's first two pages then
+    // go out before the query preparation, which runs under their latency. ----
     const int64_t bt_row = (int64_t)seq * A.max_pages;
-    // this wave's run of the split's p1 - p0 pages: the first wave on each
-    // SIMD (waves 0..kWaves/2-1) takes first_wave_pages of them, the second
-    // waves share the rest
-    constexpr int kHalf = kWaves / 2;
-    const int fpw = first_wave_pages(p1 - p0);
-    int wofs, wcnt;
-    if (wave < kHalf) {
-        wofs = wave * fpw;
-        wcnt = fpw;
-    } else {
-        const int rest = (p1 - p0) - kHalf * fpw;
-        const int per = (rest + kHalf - 1) / kHalf;
-        wofs = kHalf * fpw + (wave - kHalf) * per;
-        wcnt = max(0, min(per, rest - (wave - kHalf) * per));
-    }
-    const int wp0 = min(p0 + wofs, p1);
-    const int wp1 = min(wp0 + wcnt, p1);
     // block-table entries of a chunk: one clamped, unconditional load per lane
     auto bt_raw = [&](int c0) { return A.block_table[bt_row + min(c0 + lane, A.max_pages - 1)]; };
-    auto bt_fetch = [&](int c0) {
-        const int v = bt_raw(c0);
-        return (c0 + lane < wp1) ? v : -1;
+    // this wave's run of a split of n pages: the first wave on each SIMD
+    // (waves 0..kWaves/2-1) takes first_wave_pages(n) of them, the second
+    // waves share the rest
+    constexpr int kHalf = kWaves / 2;
+    auto wave_run = [&](int n, int &wofs, int &wcnt) {   // (selects, no branch)
+        const int fpw = first_wave_pages(n);
+        const int rest = n - kHalf * fpw;
+        const int per = (rest + kHalf - 1) / kHalf;
+        const bool first = wave < kHalf;
+        wofs = first ? wave * fpw : kHalf * fpw + (wave - kHalf) * per;
+        wcnt = first ? fpw : max(0, min(per, rest - (wave - kHalf) * per));
     };
-    const int ph_first = bt_fetch(wp0);
+    const int p0 = split * A.pps;
+    int wofs, wcnt;
+    wave_run(A.pps, wofs, wcnt);
+    int ph_raw = bt_raw(p0 + wofs);
+    int ph1_raw = TB != 0 ? bt_raw(p0 + wofs + 64) : 0;
     static_assert(kBufs >= 2, "at least one page in flight");
     // Tables and query rows to LDS: all loads first (clamped indices, no
     // branches), then the stores, so the staging costs one memory round trip.
@@ -572,6 +557,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
     for (int i = 0; i < kNQ; ++i) st_q[i] = A.q[head0 * D + min(tid + i * kThreads, G * D - 1)];
     const float st_r = A.rlev[kvh * 256 + (tid & 255)];
+    int len = A.seq_lens[seq];
+    __builtin_amdgcn_sched_barrier(0);   // (every load above is issued before the wait for len)
+
+    len = max(0, min(len, A.max_pages * kPage));
+    const int npages = (len + kPage - 1) / kPage;
+    if (p0 >= npages) {   // whole workgroup, before any barrier
+        // the loads above are consumed here too, so that they stay ahead of
+        // this branch (issued with the length load, not after it)
+        auto keep = [](auto x) { asm volatile("" ::"v"(x)); };
+        keep(ph_raw);
+        keep(ph1_raw);
+#pragma unroll
+        for (int i = 0; i < kNL; ++i) keep(st_lut[i]);
+#pragma unroll
+        for (int i = 0; i < kNT; ++i) {
+            keep(st_c2[i]);
+            keep(st_s2[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kNQ; ++i) keep(st_q[i]);
+        keep(st_r);
+        // a sequence with no resident token: its output rows are 0
+        if (npages == 0 && split == 0)
+            for (int e = threadIdx.x; e < G * D; e += kThreads) A.out[head0 * D + e] = 0.f;
+        return;
+    }
+    const int p1 = min(p0 + A.pps, npages);
+    if (p1 - p0 != A.pps) {   // the last split of its sequence: the wave's run moves
+        wave_run(p1 - p0, wofs, wcnt);
+        ph_raw = bt_raw(p0 + wofs);
+        if constexpr (TB != 0) ph1_raw = bt_raw(p0 + wofs + 64);
+    }
+    const int wp0 = min(p0 + wofs, p1);
+    const int wp1 = min(wp0 + wcnt, p1);
+    const int ph_first = (wp0 + lane < wp1) ? ph_raw : -1;
     // (the stores use the same clamped indices: a thread past the end writes
     // the last element's own value again, so every load is consumed on every
     // path and the compiler's wait counts stay exact)
@@ -702,7 +722,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         return pd;
     };
     if constexpr (TB != 0) {
-        e_ph1 = bt_raw(wp0 + 64);
+        e_ph1 = ph1_raw;
 #pragma unroll
         for (int i = 0; i < kBufs; ++i) {
             dd[i] = rdesc(i, std::integral_constant<int, 0>{});
@@ -897,7 +917,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int c0 = wp0; TB == 0 && c0 < wp1; c0 += 64) {
         if (c0 != wp0) start_chunk(c0, ph_next);
         else if (TB == 0) start_chunk(c0, ph_first);
-        ph_next = bt_fetch(c0 + 64);   // (all -1 past the wave's run)
+        ph_next = bt_raw(c0 + 64);
+        ph_next = (c0 + 64 + lane < wp1) ? ph_next : -1;   // (all -1 past the wave's run)
         if (nvalid == 0) continue;
         const int last = nvalid - 1;
         for (int k = 0; k < nvalid; k += kBufs) {

@@ -16,13 +16,13 @@ constexpr int kThreads = 64 * kWaves;
 
 // A decode workgroup holds two waves on each SIMD of its CU.  Measured on
 // MI355X, the wave dispatched first to a SIMD is served memory requests
-// ahead of the second and streams pages about 1.17x as fast, so with equal
+// ahead of the second and streams pages about 1.3x as fast, so with equal
 // page counts the second waves finish last.  The first wave on each SIMD
 // therefore takes the larger share of a chunk of n pages: round(n r / (h (1 + r)))
 // pages with r the rate ratio and h = kWaves / 2.  The shares depend on n
 // only (not on timing), so results are reproducible.
 #ifndef SKA_FIRST_WAVE_RATE_PCT
-#define SKA_FIRST_WAVE_RATE_PCT 117
+#define SKA_FIRST_WAVE_RATE_PCT 130
 #endif
 __host__ __device__ constexpr int first_wave_pages(int n) {
     constexpr int h = kWaves / 2, r = SKA_FIRST_WAVE_RATE_PCT;
