@@ -763,13 +763,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         const double xa = (double)qs[h][D - 2], ya = (double)qs[h][D - 1];   // the azimuth pair
         const bool hp = (ya < 0.0) || (ya == 0.0 && xa < 0.0);
         const double xpa = hp ? -xa : xa, ypa = hp ? -ya : ya;
+        // the exact query direction (query mode 1), the same for every tier
+        float ux[PL];
+#pragma unroll
+        for (int r = 0; r < PL; ++r) ux[r] = 0.f;
+        if (__builtin_expect(A.query_mode == 1, 0)) {
+#pragma unroll
+            for (int r = 0; r < PL; ++r) ux[r] = qn > 0.0 ? (float)((double)xr[r] / qn) : 0.f;
+        }
         int ti = 0;
-        for (int b = 2; b <= 8; ++b) {
-            if (!((A.tier_mask >> b) & 1u)) continue;
+        // the tiers present: only the kernel's own when the pool has one
+        for (int b = (TB != 0 ? TB : 2); b <= (TB != 0 ? TB : 8); ++b) {
+            if (TB == 0 && !((A.tier_mask >> b) & 1u)) continue;
             float uv[PL];
             if (A.query_mode == 1) {
 #pragma unroll
-                for (int r = 0; r < PL; ++r) uv[r] = qn > 0.0 ? (float)((double)xr[r] / qn) : 0.f;
+                for (int r = 0; r < PL; ++r) uv[r] = ux[r];
             } else {
                 // one code per component; polar and azimuth share the code path
                 int code[PL];
@@ -782,8 +791,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                     const double S = az ? ypa * ypa : Sr[r];
                     const int bb = az ? b - 1 : b;
                     bool okr;
-                    const int g = polar_code_checked(x, S, bb, c2s + thr_off(bb), s2s + thr_off(bb),
-                                                     polar_guess(x, S, bb), az ? 0.0 : 5e-14, okr);
+                    const int g = polar_code_window(x, S, bb, c2s + thr_off(bb), s2s + thr_off(bb),
+                                                    polar_guess(x, S, bb), az ? 0.0 : 5e-14, okr);
                     code[r] = g;
                     ok = ok && (a >= D - 1 || okr);
                 }
@@ -1000,14 +1009,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         float *ml = A.part_ml + row * A.nsplit * 2;
         float *po = A.part_o + row * A.nsplit * D + e;
         auto ld = [](float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-        float M = -INFINITY;
-        for (int sp = 0; sp < ns_g; ++sp) M = fmaxf(M, ld(ml + 2 * sp));
-        float O = 0.f, L = 0.f;
-        if (M != -INFINITY) {
-            for (int sp = 0; sp < ns_g; ++sp) {
-                const float sc = exp2f(ld(ml + 2 * sp) - M);
-                L += sc * ld(ml + 2 * sp + 1);
-                O += sc * ld(po + (int64_t)sp * D);
+        // kMB splits' partials are requested at once, then folded into the
+        // running (M, L, O) in split order
+        constexpr int kMB = 4;
+        float M = -INFINITY, O = 0.f, L = 0.f;
+        for (int sp0 = 0; sp0 < ns_g; sp0 += kMB) {
+            float pm[kMB], pl[kMB], pv[kMB];
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) {
+                const int sp = min(sp0 + i, ns_g - 1);
+                pm[i] = ld(ml + 2 * sp);
+                pl[i] = ld(ml + 2 * sp + 1);
+                pv[i] = ld(po + (int64_t)sp * D);
+            }
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) {
+                const float Mn = fmaxf(M, pm[i]);
+                if (sp0 + i < ns_g && Mn != -INFINITY) {
+                    const float a = exp2f(M - Mn), c = exp2f(pm[i] - Mn);
+                    L = L * a + pl[i] * c;
+                    O = O * a + pv[i] * c;
+                    M = Mn;
+                }
             }
         }
         A.out[row * D + e] = (M != -INFINITY) ? O / L : 0.f;

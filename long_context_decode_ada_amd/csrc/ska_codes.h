@@ -66,44 +66,61 @@ __device__ __forceinline__ int polar_code_near(double x, double S, int b, const 
     return g;
 }
 
-// A guess for polar_code_near: floor(atan2(sqrt(S), x) * 2^b / pi) in binary32.
-__device__ __forceinline__ int polar_guess(double x, double S, int b) {
-    const float phi = atan2f(sqrtf((float)S), (float)x);
-    return (int)(phi * (float)(1 << b) * 0.31830988618379067f);
+// A guess for the code: floor(atan2(sqrt(S), x) * 2^b / pi) from binary32
+// arithmetic with the hardware square root and reciprocal and a degree-9 odd
+// polynomial for atan on [0, 1] (fitted here, error below 1.2e-5 rad).  Its
+// error stays far below one bin (pi / 256 at 8 bits), so the code lies
+// within one of it; polar_code_window decides which exactly.
+__device__ __forceinline__ int polar_guess(double xd, double Sd, int b) {
+    const float x = (float)xd, y = __builtin_amdgcn_sqrtf((float)Sd);
+    const float ax = fabsf(x), mx = fmaxf(ax, y), mn = fminf(ax, y);
+    const float t = mx > 0.f ? mn * __builtin_amdgcn_rcpf(mx) : 0.f;   // in [0, 1]
+    const float s = t * t;
+    const float at = t * (0.99986631f + s * (-0.33030480f + s * (0.18015929f + s * (-0.085156336f + s * 0.020845106f))));
+    float phi = y > ax ? 1.57079633f - at : at;   // atan2(y, |x|)
+    phi = x < 0.f ? 3.14159265f - phi : phi;
+    return (int)(phi * (float)(1 << b) * 0.318309886f);
 }
 
-// The code from a guess g, confirmed by the two predicates around it: the
-// code is g when "phi >= theta_g" holds (or g = 0) and "phi >= theta_{g+1}"
-// fails (or g = 2^b - 1).  S may carry a relative error up to rel_err (a sum
-// taken in another order than the defining one); a product comparison whose
-// two sides differ by less than that error allows could go either way, so
-// then, as when the guess is wrong, ok is cleared and the caller must decide
-// with the exact S.  With rel_err = 0 the predicates are the defining ones.
-__device__ __forceinline__ int polar_code_checked(double x, double S, int b, const double *__restrict__ cos2,
-                                                  const double *__restrict__ sin2, int g, double rel_err, bool &ok) {
+// The code from a guess g that is off by at most one, confirmed by the
+// predicates "phi >= theta_j" at the four edges j = g-1 .. g+2: the
+// predicate holds for j = 1..code and fails above, so with it holding at
+// g-1 (or g-1 < 1) and failing at g+2 (or g+2 > 2^b - 1), the code is
+// max(g-2, 0) plus the number of edges among g-1 .. g+1 where it holds.  S
+// may carry a relative error up to rel_err (a sum taken in another order
+// than the defining one); a product comparison whose two sides differ by
+// less than that error allows could go either way, so then, as when the
+// guess is off by more, ok is cleared and the caller must decide with the
+// exact S.  With rel_err = 0 the predicates are the defining ones.
+__device__ __forceinline__ int polar_code_window(double x, double S, int b, const double *__restrict__ cos2,
+                                                 const double *__restrict__ sin2, int g, double rel_err, bool &ok) {
 #pragma clang fp contract(off)
-    // straight-line (no branches): both neighbouring edges are read and
-    // decided with selects
+    // straight-line (no branches): all four edges are read and decided with
+    // selects
     const int n = 1 << b;
     const double x2 = x * x;
     g = min(max(g, 0), n - 1);
-    const int j1 = max(g, 1), j2 = min(g + 1, n - 1);
-    const double a1 = cos2[j1] * S, c1 = sin2[j1] * x2;
-    const double a2 = cos2[j2] * S, c2 = sin2[j2] * x2;
-    auto decide = [&](int j, double a, double c, bool &sure) {
-        const bool low = 2 * j < n, mid = 2 * j == n;
+    int cnt = max(g - 2, 0);
+    bool good = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = g - 1 + i;
+        const bool inr = j >= 1 && j <= n - 1;
+        const int jc = min(max(j, 1), n - 1);
+        const double a = cos2[jc] * S, c = sin2[jc] * x2;
+        const bool low = 2 * jc < n, mid = 2 * jc == n;
         const bool prod = low ? (a >= c) : (a <= c);
         const bool by_sign = mid || (low && x <= 0.0) || (!low && x >= 0.0);
-        sure = by_sign || (fabs(a - c) > 2.0 * rel_err * a);
-        return mid ? (x <= 0.0) : (low ? (x <= 0.0 || prod) : (x < 0.0 && prod));
-    };
-    bool s1, s2;
-    const bool p1 = decide(j1, a1, c1, s1), p2 = decide(j2, a2, c2, s2);
-    const bool at = (g == 0) || p1;
-    const bool above = (g < n - 1) && p2;
+        const bool sure = by_sign || (fabs(a - c) > 2.0 * rel_err * a);
+        const bool p = mid ? (x <= 0.0) : (low ? (x <= 0.0 || prod) : (x < 0.0 && prod));
+        if (i < 3) cnt += (inr && p) ? 1 : 0;
+        good = good && (!inr || sure);
+        if (i == 0) good = good && (!inr || p);    // holds at g-1
+        if (i == 3) good = good && (!inr || !p);   // fails at g+2
+    }
     const bool zero = (x == 0.0 && S == 0.0);
-    ok = zero || (((g == 0) || s1) && ((g == n - 1) || s2) && at && !above);
-    return zero ? 0 : g;
+    ok = zero || good;
+    return zero ? 0 : cnt;
 }
 
 // Azimuth atan2(y, x) mod 2*pi at b bits: the lower half plane is turned by
@@ -122,18 +139,6 @@ __device__ __forceinline__ int azimuth_code(double x, double y, int b, const dou
 __device__ __forceinline__ double add_square(double T, float x) {
 #pragma clang fp contract(off)
     return T + (double)x * (double)x;
-}
-
-// Azimuth code through polar_code_near (same result as azimuth_code).
-__device__ __forceinline__ int azimuth_code_near(double x, double y, int b, const double *__restrict__ cos2h,
-                                                 const double *__restrict__ sin2h) {
-#pragma clang fp contract(off)
-    if (x == 0.0 && y == 0.0) return 0;
-    const bool h = (y < 0.0) || (y == 0.0 && x < 0.0);
-    const double xp = h ? -x : x;
-    const double yp = h ? -y : y;
-    const double S = yp * yp;
-    return (h ? (1 << (b - 1)) : 0) + polar_code_near(xp, S, b - 1, cos2h, sin2h, polar_guess(xp, S, b - 1));
 }
 
 }  // namespace ska
