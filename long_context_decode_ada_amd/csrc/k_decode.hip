@@ -1009,18 +1009,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         float *ml = A.part_ml + row * A.nsplit * 2;
         float *po = A.part_o + row * A.nsplit * D + e;
         auto ld = [](float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-        // kMB splits' partials are requested at once, then folded into the
-        // running (M, L, O) in split order
-        constexpr int kMB = 4;
+        // up to kMB splits' partials are requested at once, then folded into
+        // the running (M, L, O) in split order
+        constexpr int kMB = 16;
         float M = -INFINITY, O = 0.f, L = 0.f;
         for (int sp0 = 0; sp0 < ns_g; sp0 += kMB) {
             float pm[kMB], pl[kMB], pv[kMB];
 #pragma unroll
             for (int i = 0; i < kMB; ++i) {
-                const int sp = min(sp0 + i, ns_g - 1);
-                pm[i] = ld(ml + 2 * sp);
-                pl[i] = ld(ml + 2 * sp + 1);
-                pv[i] = ld(po + (int64_t)sp * D);
+                pm[i] = -INFINITY;
+                pl[i] = pv[i] = 0.f;
+                if (sp0 + i < ns_g) {
+                    const int sp = sp0 + i;
+                    pm[i] = ld(ml + 2 * sp);
+                    pl[i] = ld(ml + 2 * sp + 1);
+                    pv[i] = ld(po + (int64_t)sp * D);
+                }
             }
 #pragma unroll
             for (int i = 0; i < kMB; ++i) {
