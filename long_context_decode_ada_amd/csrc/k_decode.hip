@@ -300,19 +300,42 @@ __device__ __forceinline__ void load_page_b(const DecodeArgs &A, const PageDesc 
     }
 }
 
+// Loads of one page of any tier (pools of mixed tiers): the same
+// instructions whatever the page's width, so that the loads of the next page
+// stay in flight across the tier dispatch of the computation.  Each lane
+// reads 32 bytes from the start of its slice (KB/4 <= 32 bytes); the buffer
+// range check is per dword, so the words past the page's record block read
+// as 0 and the rest repeat bytes of the same cache lines.
+template <int D>
+__device__ __forceinline__ void load_page_any(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
+    const int lane = threadIdx.x & 63;
+    const int t = lane >> 2, j = lane & 3;
+    const int q4 = lane >> 4, n16 = lane & 15;
+    const int KB = record_bytes(D, pd.b);
+    const int64_t pk = (int64_t)pd.phys * A.hkv + kvh;
+    const int lv = __builtin_amdgcn_readfirstlane(pd.live ? 1 : 0);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + pd.off + (uint64_t)kvh * kPage * KB, lv * kPage * KB);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(A.v + pk * (int64_t)D * kPage, lv * D * kPage * 2);
+    const __amdgpu_buffer_rsrc_t rr = buf_rsrc(A.rcode + pk * kPage, lv * kPage);
+    const int vo = t * KB + j * (KB / 4);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 16 * k, 0, 0);
+        r.cw[4 * k + 0] = x[0]; r.cw[4 * k + 1] = x[1]; r.cw[4 * k + 2] = x[2]; r.cw[4 * k + 3] = x[3];
+    }
+    r.rc = __builtin_amdgcn_raw_buffer_load_b8(rr, t, 0, 0);
+    const int vv = (n16 * kPage + 4 * q4) * 2;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rv, vv + k * 16 * kPage * 2, 0, 0);
+        r.vf[k] = make_uint2(x[0], x[1]);
+    }
+}
+
 template <int D, int TB>
 __device__ __forceinline__ void load_page(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
-    if constexpr (TB != 0) {
-        load_page_b<D, TB, true>(A, pd, kvh, r);
-    } else {
-        switch (pd.b) {
-            case 2: load_page_b<D, 2, false>(A, pd, kvh, r); break;
-            case 3: load_page_b<D, 3, false>(A, pd, kvh, r); break;
-            case 4: load_page_b<D, 4, false>(A, pd, kvh, r); break;
-            case 6: load_page_b<D, 6, false>(A, pd, kvh, r); break;
-            default: load_page_b<D, 8, false>(A, pd, kvh, r); break;
-        }
-    }
+    if constexpr (TB != 0) load_page_b<D, TB, true>(A, pd, kvh, r);
+    else load_page_any<D>(A, pd, kvh, r);
 }
 
 // f_b, logits, online softmax and the MFMA P.V update of one page.  DBG also
@@ -883,7 +906,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     auto ensure_query = [&](int b) {
         if constexpr (TB == 0) {
             if (b != cur_b) {
-                load_query<D, G>(reinterpret_cast<const uint4 *>(uqw + (A.tslot[b] * 4 + jq) * (D * G / 8)), u);
+                // the tier's slot among the tiers present, in increasing width
+                const int slot = __builtin_popcount(A.tier_mask & ((1u << b) - 1u));
+                load_query<D, G>(reinterpret_cast<const uint4 *>(uqw + (slot * 4 + jq) * (D * G / 8)), u);
                 cur_b = b;
             }
         }
