@@ -969,7 +969,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         }
     }
 
-    // ---- merge the four waves of this workgroup ----
+    // ---- merge the eight waves of this workgroup ----
     const float lsum = head_reduce<G, false>(st.l);
     if (lane < G) {
         mml[wave][lane][0] = st.m;
