@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // query preparation: the G query rows, their suffix sums, the edge tables
     // of the tiers present, and the resulting packed unit directions
     __shared__ float qs[G][D];
-    __shared__ double qT[G][D];
+    __shared__ double qT[kWaves][D];
     __shared__ double c2s[kThrEntries], s2s[kThrEntries];
     __shared__ __attribute__((aligned(16))) _Float16 uq_lds[(TB == 0 ? 5 : 1) * D * G];
     __shared__ float sq_lds[G];
@@ -757,14 +757,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
     // Query prep, section 2.1's c_q: per tier, the angle codes of each query
     // row and the decoded direction u_a = (prod_{k<a} sin c_k) * cos c_a
-    // (one wave per head, D/64 components per lane).  The suffix sums of
-    // squares the codes compare against are taken by a wave scan (fast, but
-    // in another order than the keys' backward sum); a code is accepted only
-    // when its decisions hold with a margin covering that reordering.  Any
-    // decision inside the margin sends the wave to the exact backward sum and
-    // the plain search, so the codes always equal the defining ones.
-    if (wave < G) {
-        const int h = wave;
+    // (D/64 components per lane).  One wave per head and tier: with a
+    // single tier waves 0..G-1, with mixed tiers all kWaves/G waves of a head,
+    // each taking every (kWaves/G)-th tier.  The suffix sums of squares the
+    // codes compare against are taken by a wave scan (fast, but in another
+    // order than the keys' backward sum); a code is accepted only when its
+    // decisions hold with a margin covering that reordering.  Any decision
+    // inside the margin sends the wave to the exact backward sum and the
+    // plain search, so the codes always equal the defining ones.
+    constexpr int kWpH = kWaves / G;   // waves per head
+    static_assert(kWaves % G == 0, "heads divide the waves");
+    if (TB == 0 || wave < G) {
+        const int h = wave % G, part = wave / G;
         constexpr int PL = D / 64;   // components per lane: a = lane * PL + r
         float xr[PL];
 #pragma unroll
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         }
         const double T0 = readlane_d(t, 0);   // |q|^2
         const double qn = sqrt(T0);
-        if (lane == 0) sq_lds[h] = (float)((double)A.scale * qn * 1.4426950408889634);
+        if (lane == 0 && part == 0) sq_lds[h] = (float)((double)A.scale * qn * 1.4426950408889634);
         const double xa = (double)qs[h][D - 2], ya = (double)qs[h][D - 1];   // the azimuth pair
         const bool hp = (ya < 0.0) || (ya == 0.0 && xa < 0.0);
         const double xpa = hp ? -xa : xa, ypa = hp ? -ya : ya;
@@ -798,6 +802,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         // the tiers present: only the kernel's own when the pool has one
         for (int b = (TB != 0 ? TB : 2); b <= (TB != 0 ? TB : 8); ++b) {
             if (TB == 0 && !((A.tier_mask >> b) & 1u)) continue;
+            if (TB == 0 && ti % kWpH != part) {   // another wave of this head takes it
+                ++ti;
+                continue;
+            }
             float uv[PL];
             if (A.query_mode == 1) {
 #pragma unroll
@@ -824,7 +832,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                     if (lane == 0) {
                         double T = 0.0;
                         for (int a2 = D - 1; a2 >= 0; --a2) {
-                            qT[h][a2] = T;   // sum over k > a2
+                            qT[wave][a2] = T;   // sum over k > a2
                             T = add_square(T, qs[h][a2]);
                         }
                     }
@@ -832,7 +840,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                     for (int r = 0; r < PL; ++r) {
                         const int a = lane * PL + r;
                         if (a < D - 2) {
-                            const double x = (double)xr[r], S = qT[h][a];
+                            const double x = (double)xr[r], S = qT[wave][a];
                             code[r] = polar_code_near(x, S, b, c2s + thr_off(b), s2s + thr_off(b), code[r]);
                         } else if (a == D - 2) {
                             code[r] = polar_code_near(xpa, ypa * ypa, b - 1, c2s + thr_off(b - 1), s2s + thr_off(b - 1),
