@@ -1109,6 +1109,8 @@ hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s
     return hipGetLastError();
 }
 
+int decode_workgroups_per_cu() { return 8 / kWaves; }
+
 __global__ void k_zero_u32(uint32_t *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;

@@ -379,7 +379,7 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
         pps = (max_pages + num_splits - 1) / num_splits;
     } else {
         const int64_t total = (int64_t)batch * hkv * max_pages;
-        const int64_t target = (int64_t)c->num_cus;  // workgroups: one per CU
+        const int64_t target = (int64_t)c->num_cus * decode_workgroups_per_cu();   // one round of resident workgroups
         pps = (int)std::min<int64_t>((total + target - 1) / target, max_pages);
         if (pps >= max_pages) pps = std::max(kMinSplitPages, (max_pages + kTailSplits - 1) / kTailSplits);
     }

@@ -115,6 +115,8 @@ hipError_t launch_calibrate(const float *keys, int64_t n, int hkv, int d, unsign
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
+// decode workgroups resident per CU (two waves per SIMD in all)
+int decode_workgroups_per_cu();
 
 
 }  // namespace ska

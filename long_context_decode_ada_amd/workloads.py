@@ -156,14 +156,20 @@ def _streams(idx: int, n: int = 10):
     return [np.random.default_rng(c) for c in ss.spawn(n)]
 
 
-def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool = True) -> Workload:
+def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool = True,
+         tiers: Optional[tuple] = None) -> Workload:
     """Build one workload.  ``scale`` < 1 shrinks the context (and, for
     ragged_b64, the lengths) for oracle-sized tests; ``batch`` overrides B;
-    ``data=False`` builds the page structure only (empty keys/values/query).
+    ``data=False`` builds the page structure only (empty keys/values/query);
+    ``tiers`` (mixed_tiers only) replaces the tier set {2,4,6,8} by the given
+    widths, drawn with equal probability (the sink page takes the widest).
     Every part draws from its own seeded stream, so the structure does not
     depend on ``data``."""
     if name not in NAMES:
         raise KeyError(name)
+    if tiers is not None and name != "mixed_tiers":
+        raise ValueError("tiers applies to mixed_tiers only")
+    tiers_override = tiers
     idx = NAMES.index(name)
     r_keys, r_vals, r_q, r_len, r_pages, r_tier, r_evict, r_scale, _, _ = _streams(idx)
 
@@ -182,6 +188,8 @@ def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool 
         lens = np.full(B, T, np.int32)
         mode = LOG
         tiers = {"gqa_t32k": {4}, "long_t128k": {3}, "mixed_tiers": {2, 4, 6, 8}}[name]
+        if tiers_override is not None:
+            tiers = set(tiers_override)
     else:  # ragged_b64
         d, hq, hkv, B = 128, 32, 8, 64
         B = batch or B
@@ -196,8 +204,11 @@ def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool 
         if name == "mixed_tiers":
             T = int(lens[s])
             npg = (T + PAGE - 1) // PAGE
-            tier = r_tier.choice(np.array([2, 4, 6, 8]), size=npg, p=[0.3, 0.4, 0.2, 0.1])
-            tier[0] = 8                                   # sink page: protected, b_max
+            if tiers_override is None:
+                tier = r_tier.choice(np.array([2, 4, 6, 8]), size=npg, p=[0.3, 0.4, 0.2, 0.1])
+            else:
+                tier = r_tier.choice(np.array(sorted(tiers)), size=npg)
+            tier[0] = max(tiers)                          # sink page: protected, b_max
             nonsink = np.arange(1, npg)
             evict = r_evict.choice(nonsink, size=len(nonsink) // 2, replace=False)
             keep = np.setdiff1d(np.arange(npg), evict)    # sorted: logical order kept

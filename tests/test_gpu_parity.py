@@ -149,3 +149,31 @@ def test_queries_and_keys_on_bin_edges():
         for k in ("kcode", "rcode", "v"):
             assert np.array_equal(g["pools"][k], o["pools"][k]), (name, k)
         compare(w, g, o, rng, q=q, label="%s edges" % name)
+
+
+def test_mixed_pool_with_all_five_tiers():
+    """A pool holding pages of every width {2, 3, 4, 6, 8}: the mixed-tier
+    kernel's loads are the same for every width (a 3-bit page has 12-byte
+    slices, read with the same 32 bytes per lane as the others)."""
+    w = W.make("mixed_tiers", 1 / 16, batch=4, tiers=(2, 3, 4, 6, 8))
+    assert set(np.unique(w.page_bits).tolist()) == {2, 3, 4, 6, 8}
+    rng = O.calibrate(w.keys)
+    g = gpu_run(w)
+    o = oracle_run(w, rng)
+    for k in ("kcode", "rcode", "v"):
+        assert np.array_equal(g["pools"][k], o["pools"][k]), k
+    assert g["errors"] == 0
+    compare(w, g, o, rng, label="five tiers")
+
+
+def test_more_splits_than_one_merge_round():
+    """64 splits of one (sequence, KV head) group: the merging workgroup folds
+    the partials in two rounds of requests; the result matches the oracle and
+    the default split count."""
+    w = W.make("long_t128k", 1 / 8)                 # B = 1, T = 16384: 1024 pages
+    rng = O.calibrate(w.keys)
+    o = oracle_run(w, rng)
+    g64 = gpu_run(w, num_splits=64)
+    compare(w, g64, o, rng, label="64 splits")
+    g0 = gpu_run(w)
+    assert np.abs(g64["out"] - g0["out"]).max() < 1e-4
