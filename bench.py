@@ -199,6 +199,7 @@ def main():
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": "k_decode<d=%d,G=%d>" % (w.d, w.hq // w.hkv), "kernel_us": round(k_ms * 1e3, 2),
+            "kernel_us_p10_p50_p90": [round(float(np.percentile(prof, p)) * 1e3, 2) for p in (10, 50, 90)],
             "alg_bytes_per_launch": int(kb)}
 
     cpu = None
