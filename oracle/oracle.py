@@ -74,6 +74,10 @@ def lib():
         L.ora_decode.restype = i
         L.ora_decode.argtypes = [i, i, i, P, P, P, i, P, P, P, P, i, i, P, i, P, d, i,
                                  P, P, P, i, i]
+        L.ora_decoded_keys.restype = i
+        L.ora_decoded_keys.argtypes = [i, i, i, P, P, P, i, P, P, P, i, P]
+        L.ora_dense_decode.restype = i
+        L.ora_dense_decode.argtypes = [i, i, P, P, P, i, i, P, i, P, d, P, P, i]
         L.ora_max_threads.restype = i
         _lib = L
     return _lib
@@ -219,6 +223,43 @@ def decode(pools: dict, radius_mode: int, rng, q, block_table, seq_lens, scale: 
                          query_mode, _p(out), _p(logits), _p(pr), npairs, int(nthreads))
     if r:
         raise ValueError("ora_decode: bad argument")
+    return (out, logits) if want_logits else out
+
+
+def decoded_keys(pools: dict, radius_mode: int, rng, phys):
+    """The dense keys k~ = r~ * u(codes) the stored records stand for, for the
+    physical pages `phys`: [len(phys)][hkv][16][d] binary64."""
+    phys = _c(phys, np.int32)
+    rng = _c(rng, np.float64)
+    d, hkv = pools["d"], pools["hkv"]
+    out = np.zeros((phys.shape[0], hkv, PAGE, d), np.float64)
+    r = lib().ora_decoded_keys(d, hkv, radius_mode, _p(rng), _p(pools["page_bits"]), _p(pools.get("page_off")),
+                               pools["bstride"], _p(pools["kcode"]), _p(pools["rcode"]), _p(phys),
+                               phys.shape[0], _p(out))
+    if r:
+        raise ValueError("ora_decoded_keys: bad page header")
+    return out
+
+
+def dense_decode(k_dense, v, q, block_table, seq_lens, scale: float = 0.0, want_logits: bool = False,
+                 nthreads: int = 0):
+    """Dense paged attention by the plain definition: keys bf16 bits
+    k_dense [num_pages][hkv][16][d], values v bf16 bits [num_pages][hkv][d][16].
+    Returns out [B][hq][d] (fp32) and, if asked, logits (natural units)."""
+    k_dense = _c(k_dense, np.uint16)
+    v = _c(v, np.uint16)
+    q = _c(q, np.float32)
+    B, hq, d = q.shape
+    hkv = k_dense.shape[1]
+    block_table = _c(block_table, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    max_pages = block_table.shape[1]
+    out = np.full((B, hq, d), np.nan, np.float32)
+    logits = np.full((B, hq, max_pages * PAGE), np.nan, np.float32) if want_logits else None
+    r = lib().ora_dense_decode(d, hkv, _p(k_dense), _p(v), _p(q), B, hq, _p(block_table), max_pages,
+                               _p(seq_lens), float(scale), _p(out), _p(logits), int(nthreads))
+    if r:
+        raise ValueError("ora_dense_decode: bad argument")
     return (out, logits) if want_logits else out
 
 

@@ -544,6 +544,113 @@ int ora_decode(int d, int hkv, int radius_mode, const double *range,
     return bad;
 }
 
+/* ------------------------------------------------------------------------ */
+/* The "decompress" step of decompress-then-dot [SKV 1]: the dense key each
+ * stored record stands for, k~ = r~ * u(centres(c)) [SKV 2.1], for the 16
+ * slots and every KV head of the given physical pages.  out [n][hkv][16][d]
+ * binary64 (page i of phys_list at out + i*hkv*16*d).  Returns 0, or 1 on a
+ * bad header. */
+int ora_decoded_keys(int d, int hkv, int radius_mode, const double *range,
+                     const uint8_t *page_bits, const uint64_t *page_off, int bstride,
+                     const uint8_t *kcode, const uint8_t *rcode,
+                     const int32_t *phys_list, int n, double *out)
+{
+    int bad = 0;
+    int32_t codes[1024];
+    double u[1024], level[256], tau2[255];
+    for (int i = 0; i < n; ++i) {
+        int64_t phys = phys_list[i];
+        int b = page_bits[phys];
+        if (b < 1 || b > 8) {
+            bad = 1;
+            continue;
+        }
+        int kb = ora_kb(d, b);
+        for (int g = 0; g < hkv; ++g) {
+            ora_radius_tables(radius_mode, range[2 * g], range[2 * g + 1], level, tau2);
+            for (int slot = 0; slot < ORA_PAGE; ++slot) {
+                const uint8_t *rec = kcode + page_base(phys, hkv, d, page_off, bstride) + ((size_t)g * ORA_PAGE + slot) * kb;
+                ora_unpack(rec, d, b, codes);
+                ora_direction(codes, d, b, u);
+                double r = level[rcode[((size_t)phys * hkv + g) * ORA_PAGE + slot]];
+                double *o = out + (((size_t)i * hkv + g) * ORA_PAGE + slot) * d;
+                for (int e = 0; e < d; ++e)
+                    o[e] = r * u[e];
+            }
+        }
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense paged attention, the baseline ADA replaces [SKV 1]: keys stored as
+ * bf16 in pages, k_dense [num_pages][hkv][16][d] (token-major), values as in
+ * the ADA pools.  For sequence s and query head h (KV head g = h/(hq/hkv)):
+ *   l_t = scale * sum_e q_e k_t,e   over the resident tokens,
+ * then softmax and the value-weighted sum; every bf16 input is converted to
+ * binary64 exactly.  out [B][hq][d]; logits as in ora_decode or NULL.
+ * Returns 0, or 1 on a bad argument. */
+int ora_dense_decode(int d, int hkv, const uint16_t *k_dense, const uint16_t *v,
+                     const float *q, int B, int hq, const int32_t *block_table, int max_pages,
+                     const int32_t *seq_lens, double scale, float *out, float *logits, int nthreads)
+{
+    if (d < 1 || hkv <= 0 || hq <= 0 || hq % hkv != 0 || B < 0)
+        return 1;
+    if (scale == 0.0)
+        scale = 1.0 / sqrt((double)d);
+    int grp = hq / hkv;
+    int64_t njobs = (int64_t)B * hq;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t job = 0; job < njobs; ++job) {
+        int s = (int)(job / hq), h = (int)(job % hq), g = h / grp;
+        int n = seq_lens[s];
+        const float *qv = q + ((size_t)s * hq + h) * d;
+        float *o = out + ((size_t)s * hq + h) * d;
+        if (n <= 0) {
+            for (int e = 0; e < d; ++e)
+                o[e] = 0.0f;
+            continue;
+        }
+        double *l = malloc(sizeof(double) * (size_t)n);
+        for (int t = 0; t < n; ++t) {
+            int64_t phys = block_table[(size_t)s * max_pages + t / ORA_PAGE];
+            int slot = t % ORA_PAGE;
+            const uint16_t *k = k_dense + (((size_t)phys * hkv + g) * ORA_PAGE + slot) * d;
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot += (double)qv[e] * bf16_to_double(k[e]);
+            l[t] = scale * dot;
+            if (logits)
+                logits[((size_t)s * hq + h) * (size_t)max_pages * ORA_PAGE + t] = (float)l[t];
+        }
+        double m = l[0];
+        for (int t = 1; t < n; ++t)
+            if (l[t] > m)
+                m = l[t];
+        double den = 0.0;
+        double *num = calloc((size_t)d, sizeof(double));
+        for (int t = 0; t < n; ++t) {
+            double w = exp(l[t] - m);
+            int64_t phys = block_table[(size_t)s * max_pages + t / ORA_PAGE];
+            int slot = t % ORA_PAGE;
+            den += w;
+            for (int e = 0; e < d; ++e)
+                num[e] += w * bf16_to_double(v[(((size_t)phys * hkv + g) * d + e) * ORA_PAGE + slot]);
+        }
+        for (int e = 0; e < d; ++e)
+            o[e] = (float)(num[e] / den);
+        free(num);
+        free(l);
+    }
+    return 0;
+}
+
 int ora_max_threads(void)
 {
 #ifdef _OPENMP
