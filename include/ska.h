@@ -137,6 +137,33 @@ ska_status ska_decode_attention(ska_cache *cache, const float *q, int batch, int
                                 const int32_t *seq_lens, float scale, int num_splits,
                                 float *out, float *logits_dbg, void *stream);
 
+/* ska_dense_decode_attention -- the baseline the codes replace (section 1 of
+ * the page: decode streams dense KV pages from HBM): the same decode step as
+ * ska_decode_attention over keys stored densely as bf16, with the cache's
+ * values, workspace and split policy; the logits are the plain
+ *     l_t = scale * sum_e q_e k_t,e
+ * (no codes, no radius).  For comparing bytes and time on the same pages.
+ *   k_dense  device bf16 [num_pages][Hkv][16][d]: token-major within a page
+ *            (the 16 slots of one KV head, d values each), filled by the
+ *            caller or by ska_decompress_keys; read, never written
+ *   other arguments as ska_decode_attention.
+ * Returns SKA_ERR_INVALID for a NULL k_dense; errors as ska_decode_attention. */
+ska_status ska_dense_decode_attention(ska_cache *cache, const uint16_t *k_dense, const float *q, int batch,
+                                      int num_q_heads, const int32_t *block_table, int max_pages,
+                                      const int32_t *seq_lens, float scale, int num_splits, float *out,
+                                      float *logits_dbg, void *stream);
+
+/* ska_decompress_keys -- the "decompress" step of the decompress-then-dot
+ * path that section 1 of the page sets against ADA: writes the dense key
+ * each stored record stands for, r~ * u(c) (section 2.1), rounded to bf16,
+ * for every slot of every resident page (pages 0 .. ceil(seq_lens[s]/16)-1 of
+ * each row of the block table) and every KV head, into k_dense (layout as in
+ * ska_dense_decode_attention; other pages are left untouched).  Pages whose
+ * id or header is out of range are skipped and flagged (ska_device_errors).
+ * batch and max_pages are at most 65535.  Returns SKA_OK. */
+ska_status ska_decompress_keys(ska_cache *cache, const int32_t *block_table, int batch, int max_pages,
+                               const int32_t *seq_lens, uint16_t *k_dense, void *stream);
+
 /* The radius range in use (host [Hkv][2] = (R_lo, R_hi)). */
 ska_status ska_get_radius_range(const ska_cache *cache, double *range_out);
 

@@ -74,6 +74,8 @@ constexpr float kLn2 = 0.69314718055994531f;
 #define SKA_WAVES_PER_SIMD 2
 #endif
 constexpr int kBufs = SKA_BUFS;
+// kernel variant reading dense bf16 keys (the baseline the codes replace)
+constexpr int kDenseTB = 16;
 constexpr int kWavesPerSimd = SKA_WAVES_PER_SIMD;
 
 // DPP quad permutations (within groups of 4 lanes).
@@ -223,6 +225,12 @@ __device__ __forceinline__ float fma_mix_hi(uint32_t u, float w, float acc) {
     return r;
 }
 
+// binary32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 struct WaveState {
     float m;     // running max (log2 units) of this lane's head
     float l;     // this lane's share of the softmax denominator
@@ -236,6 +244,7 @@ struct PageBuf {
     uint32_t rc;
     uint32_t hb;   // the page header (its angle bit width), single-tier kernels
     uint2 vf[D / 16];
+    uint2 kf[D / 16];   // dense keys: the MFMA B operand of Q.K^T
 };
 
 // Wave-uniform description of one page.
@@ -332,87 +341,62 @@ __device__ __forceinline__ void load_page_any(const DecodeArgs &A, const PageDes
     }
 }
 
+// Loads of one page of dense bf16 keys and its values.  Keys are token-major
+// ([16][d] per (page, KV head)); the lane takes the four dimensions
+// 16k + 4(l/16) .. +3 of token l%16 for each k, the B operand of a 16x16x16
+// MFMA over (dimension, token).
+template <int D>
+__device__ __forceinline__ void load_page_dense(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
+    const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4, n16 = lane & 15;
+    const int64_t pk = (int64_t)pd.phys * A.hkv + kvh;
+    const int lv = __builtin_amdgcn_readfirstlane(pd.live ? 1 : 0);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kdense + pk * (int64_t)kPage * D, lv * kPage * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(A.v + pk * (int64_t)D * kPage, lv * D * kPage * 2);
+    const int ko = (n16 * D + 4 * q4) * 2;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rk, ko + 32 * k, 0, 0);
+        r.kf[k] = make_uint2(x[0], x[1]);
+    }
+    const int vv = (n16 * kPage + 4 * q4) * 2;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rv, vv + k * 16 * kPage * 2, 0, 0);
+        r.vf[k] = make_uint2(x[0], x[1]);
+    }
+}
+
 template <int D, int TB>
 __device__ __forceinline__ void load_page(const DecodeArgs &A, const PageDesc &pd, int kvh, PageBuf<D> &r) {
-    if constexpr (TB != 0) load_page_b<D, TB, true>(A, pd, kvh, r);
+    if constexpr (TB == kDenseTB) load_page_dense<D>(A, pd, kvh, r);
+    else if constexpr (TB != 0) load_page_b<D, TB, true>(A, pd, kvh, r);
     else load_page_any<D>(A, pd, kvh, r);
 }
 
-// f_b, logits, online softmax and the MFMA P.V update of one page.  DBG also
-// stores the logits (a separate kernel variant, so that the store does not
-// enter the memory-wait accounting of the production loop).
-template <int D, int G, int B, bool DBG>
-__device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &r, int ntok, int64_t logit_base,
-                                               const uint32_t (&u)[D * G / 8], float sq, const float2 *__restrict__ lut,
-                                               const float *__restrict__ rlev, float *__restrict__ pb,
-                                               WaveState &st, v4f (&acc)[D / 16]) {
-    constexpr int NA = D / 4;
+// The product of the sine products P of the slices before this lane's slice
+// j within its token's four lanes (exclusive quad scan): C_j = prod_{i<j} P_i.
+__device__ __forceinline__ float slice_prefix(float P, int j) {
+    float C = qperm<kQuadShr1>(P);
+    C = (j == 0) ? 1.f : C;
+    const float z = qperm<kQuadShr1>(C);
+    C = (j >= 1) ? C * z : C;
+    const float z2 = qperm<kQuadShr2>(C);
+    C = (j >= 2) ? C * z2 : C;
+    return C;
+}
+
+// Online softmax of one page's logits lg (log2 units; lane 4t + j holds token
+// t for head j % G) and the MFMA update of the G output rows with the page's
+// values.  DBG also stores the logits.
+template <int D, int G, bool DBG>
+__device__ __forceinline__ void softmax_pv(const DecodeArgs &A, float lg, int ntok, int64_t logit_base,
+                                           uint2 (&vf)[D / 16], float *__restrict__ pb, WaveState &st,
+                                           v4f (&acc)[D / 16]) {
     constexpr int NT = D / 16;
     const int lane = threadIdx.x & 63;
     const int t = lane >> 2, j = lane & 3;
     const int q4 = lane >> 4, n16 = lane & 15;
-
-    // ---- f_b on the lane's slice ----
-    const uint32_t az_base = 8u * ((j == 3) ? lut_azimuth(B) : lut_polar(B));
-    const uint32_t pad_base = 8u * ((j == 3) ? kLutOnes : lut_polar(B));
-    const char *lutb = reinterpret_cast<const char *>(lut);
-    CodeAddr<B> ca;
-    ca.init(r.cw);
-    float F[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) F[h] = 0.f;
-    float P = 1.f;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-        const uint32_t c8 = ca.at(r.cw, i);
-        uint32_t e8;
-        if (i == NA - 2) e8 = az_base + c8;
-        else if (i == NA - 1) e8 = pad_base + c8;
-        else e8 = 8u * lut_polar(B) + c8;
-        const float2 cs = *reinterpret_cast<const float2 *>(lutb + e8);
-        const float w = P * cs.x;
-        P = P * cs.y;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const int e2 = i * G + h;   // element (angle i, head h) of the packed halves
-            F[h] = (e2 & 1) ? fma_mix_hi(u[e2 >> 1], w, F[h]) : fma_mix_lo(u[e2 >> 1], w, F[h]);
-        }
-    }
-
-    // ---- join the four slices: C_j = prod_{i<j} S_i ----
-    float C = qperm<kQuadShr1>(P);
-    C = (j == 0) ? 1.f : C;
-    {
-        const float z = qperm<kQuadShr1>(C);
-        C = (j >= 1) ? C * z : C;
-        const float z2 = qperm<kQuadShr2>(C);
-        C = (j >= 2) ? C * z2 : C;
-    }
-    float f;
-    if constexpr (G == 4) {
-        const float X0 = C * F[0], X1 = C * F[1], X2 = C * F[2], X3 = C * F[3];
-        const bool odd = j & 1;
-        const float s0 = odd ? X0 : X1, k0 = odd ? X1 : X0;
-        const float s1 = odd ? X2 : X3, k1 = odd ? X3 : X2;
-        const float Y0 = k0 + qperm<kQuadXor1>(s0);
-        const float Y1 = k1 + qperm<kQuadXor1>(s1);
-        const bool hi2 = j & 2;
-        const float s2 = hi2 ? Y0 : Y1, k2 = hi2 ? Y1 : Y0;
-        f = k2 + qperm<kQuadXor2>(s2);
-    } else if constexpr (G == 2) {
-        const float X0 = C * F[0], X1 = C * F[1];
-        const bool odd = j & 1;
-        const float s0 = odd ? X0 : X1, k0 = odd ? X1 : X0;
-        const float Y = k0 + qperm<kQuadXor1>(s0);
-        f = Y + qperm<kQuadXor2>(Y);
-    } else {
-        const float X = C * F[0];
-        const float Y = X + qperm<kQuadXor1>(X);
-        f = Y + qperm<kQuadXor2>(Y);
-    }
-
-    // ---- logits (log2 units) and online softmax ----
-    const float lg = (t < ntok) ? sq * rlev[r.rc] * f : -INFINITY;
     if constexpr (DBG) {
         if (j < G && t < ntok) A.logits[logit_base + (int64_t)j * A.max_pages * kPage + t] = lg * kLn2;
     }
@@ -456,24 +440,133 @@ __device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &
         const uint32_t m0 = (base + 0 < ntok ? 0x0000FFFFu : 0u) | (base + 1 < ntok ? 0xFFFF0000u : 0u);
         const uint32_t m1 = (base + 2 < ntok ? 0x0000FFFFu : 0u) | (base + 3 < ntok ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int k = 0; k < NT; ++k) { r.vf[k].x &= m0; r.vf[k].y &= m1; }
+        for (int k = 0; k < NT; ++k) { vf[k].x &= m0; vf[k].y &= m1; }
     }
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
         v4s bfr;
-        __builtin_memcpy(&bfr, &r.vf[k], 8);
+        __builtin_memcpy(&bfr, &vf[k], 8);
         acc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(af, bfr, acc[k], 0, 0, 0);
     }
 }
 
+
+// f_b, logits, online softmax and the MFMA P.V update of one page.  DBG also
+// stores the logits (a separate kernel variant, so that the store does not
+// enter the memory-wait accounting of the production loop).
+template <int D, int G, int B, bool DBG>
+__device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &r, int ntok, int64_t logit_base,
+                                               const uint32_t (&u)[D * G / 8], float sq, const float2 *__restrict__ lut,
+                                               const float *__restrict__ rlev, float *__restrict__ pb,
+                                               WaveState &st, v4f (&acc)[D / 16]) {
+    constexpr int NA = D / 4;
+    constexpr int NT = D / 16;
+    const int lane = threadIdx.x & 63;
+    const int t = lane >> 2, j = lane & 3;
+    const int q4 = lane >> 4, n16 = lane & 15;
+
+    // ---- f_b on the lane's slice ----
+    const uint32_t az_base = 8u * ((j == 3) ? lut_azimuth(B) : lut_polar(B));
+    const uint32_t pad_base = 8u * ((j == 3) ? kLutOnes : lut_polar(B));
+    const char *lutb = reinterpret_cast<const char *>(lut);
+    CodeAddr<B> ca;
+    ca.init(r.cw);
+    float F[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) F[h] = 0.f;
+    float P = 1.f;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const uint32_t c8 = ca.at(r.cw, i);
+        uint32_t e8;
+        if (i == NA - 2) e8 = az_base + c8;
+        else if (i == NA - 1) e8 = pad_base + c8;
+        else e8 = 8u * lut_polar(B) + c8;
+        const float2 cs = *reinterpret_cast<const float2 *>(lutb + e8);
+        const float w = P * cs.x;
+        P = P * cs.y;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const int e2 = i * G + h;   // element (angle i, head h) of the packed halves
+            F[h] = (e2 & 1) ? fma_mix_hi(u[e2 >> 1], w, F[h]) : fma_mix_lo(u[e2 >> 1], w, F[h]);
+        }
+    }
+
+    // ---- join the four slices: C_j = prod_{i<j} S_i ----
+    const float C = slice_prefix(P, j);
+    float f;
+    if constexpr (G == 4) {
+        const float X0 = C * F[0], X1 = C * F[1], X2 = C * F[2], X3 = C * F[3];
+        const bool odd = j & 1;
+        const float s0 = odd ? X0 : X1, k0 = odd ? X1 : X0;
+        const float s1 = odd ? X2 : X3, k1 = odd ? X3 : X2;
+        const float Y0 = k0 + qperm<kQuadXor1>(s0);
+        const float Y1 = k1 + qperm<kQuadXor1>(s1);
+        const bool hi2 = j & 2;
+        const float s2 = hi2 ? Y0 : Y1, k2 = hi2 ? Y1 : Y0;
+        f = k2 + qperm<kQuadXor2>(s2);
+    } else if constexpr (G == 2) {
+        const float X0 = C * F[0], X1 = C * F[1];
+        const bool odd = j & 1;
+        const float s0 = odd ? X0 : X1, k0 = odd ? X1 : X0;
+        const float Y = k0 + qperm<kQuadXor1>(s0);
+        f = Y + qperm<kQuadXor2>(Y);
+    } else {
+        const float X = C * F[0];
+        const float Y = X + qperm<kQuadXor1>(X);
+        f = Y + qperm<kQuadXor2>(Y);
+    }
+
+    // ---- logits (log2 units), online softmax and P.V ----
+    const float lg = (t < ntok) ? sq * rlev[r.rc] * f : -INFINITY;
+    softmax_pv<D, G, DBG>(A, lg, ntok, logit_base, r.vf, pb, st, acc);
+}
+
+// Dense keys: the page's logits S = Q.K^T on MFMA (query rows, the G heads
+// padded to 16, as the A operand, split exactly into bf16 hi + lo halves:
+// qd[4k], qd[4k+1] hold the hi pairs of dimensions 16k + 4(l/16) .. +3 of
+// head l%16, qd[4k+2], qd[4k+3] the lo pairs), then the same softmax and
+// P.V as the coded kernels.
+template <int D, int G, bool DBG>
+__device__ __forceinline__ void compute_page_dense(const DecodeArgs &A, PageBuf<D> &r, int ntok, int64_t logit_base,
+                                                   const uint32_t (&qd)[D / 4], float sq, float *__restrict__ pb,
+                                                   WaveState &st, v4f (&acc)[D / 16]) {
+    const int lane = threadIdx.x & 63;
+    const int t = lane >> 2, j = lane & 3;
+    v4f s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+        v4s bk, ah, al;
+        __builtin_memcpy(&bk, &r.kf[k], 8);
+        __builtin_memcpy(&ah, &qd[4 * k], 8);
+        __builtin_memcpy(&al, &qd[4 * k + 2], 8);
+        s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bk, s4, 0, 0, 0);
+        s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bk, s4, 0, 0, 0);
+    }
+    // S[h][token n] sits in lane n (h < 4), element h; lane 4t + j takes head
+    // j % G of token t
+    const int src = t * 4;
+    const float e0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(s4.x)));
+    const float e1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(s4.y)));
+    const float e2 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(s4.z)));
+    const float e3 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(s4.w)));
+    const int hj = j % G;
+    const float f = hj == 0 ? e0 : hj == 1 ? e1 : hj == 2 ? e2 : e3;
+    const float lg = (t < ntok) ? sq * f : -INFINITY;
+    softmax_pv<D, G, DBG>(A, lg, ntok, logit_base, r.vf, pb, st, acc);
+}
+
 template <int D, int G, int TB, bool DBG>
 __device__ __forceinline__ void compute_page(const DecodeArgs &A, const PageDesc &pd, PageBuf<D> &r, int len,
-                                             int64_t head0, const uint32_t (&u)[D * G / 8], float sq,
+                                             int64_t head0, const uint32_t (&u)[D * G / 8],
+                                             const uint32_t (&qd)[D / 4], float sq,
                                              const float2 *__restrict__ lut, const float *__restrict__ rlev,
                                              float *__restrict__ pb, WaveState &st, v4f (&acc)[D / 16]) {
     const int ntok = min(kPage, len - pd.p * kPage);
     const int64_t lbase = head0 * A.max_pages * kPage + (int64_t)pd.p * kPage;
-    if constexpr (TB != 0) {
+    if constexpr (TB == kDenseTB) {
+        compute_page_dense<D, G, DBG>(A, r, ntok, lbase, qd, sq, pb, st, acc);
+    } else if constexpr (TB != 0) {
         // a page whose header disagrees with the kernel's tier is flagged and skipped
         if (__builtin_amdgcn_readfirstlane(r.hb) != TB) {
             if ((threadIdx.x & 63) == 0) atomicOr(A.err, 4u);
@@ -767,7 +860,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // plain search, so the codes always equal the defining ones.
     constexpr int kWpH = kWaves / G;   // waves per head
     static_assert(kWaves % G == 0, "heads divide the waves");
-    if (TB == 0 || wave < G) {
+    if (TB != kDenseTB && (TB == 0 || wave < G)) {
         const int h = wave % G, part = wave / G;
         constexpr int PL = D / 64;   // components per lane: a = lane * PL + r
         float xr[PL];
@@ -897,18 +990,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
     for (int k = 0; k < NT; ++k) acc[k] = v4f{0.f, 0.f, 0.f, 0.f};
     uint32_t u[D * G / 8];
+    uint32_t qd[D / 4];   // dense keys: the query rows as MFMA A operands (bf16 hi, lo)
     int cur_b = -1;
     const int jq = lane & 3;
     const uint32_t *uqw = reinterpret_cast<const uint32_t *>(uq_lds);
-    if constexpr (TB != 0) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) qd[i] = 0u;
+    if constexpr (TB == kDenseTB) {
+#pragma unroll
+        for (int i = 0; i < D * G / 8; ++i) u[i] = 0u;
+        // lane l: head l%16 (rows past G stay 0), dimensions 16k + 4(l/16) .. +3
+        const int hq_row = lane & 15;
+        if (hq_row < G) {
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) {
+                uint32_t hi2[2], lo2[2];
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    uint32_t hb[2], lb[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float x = qs[hq_row][16 * k + 4 * (lane >> 4) + 2 * m + e];
+                        hb[e] = bf16_rne(x);
+                        lb[e] = bf16_rne(x - __uint_as_float(hb[e] << 16));
+                    }
+                    hi2[m] = hb[0] | (hb[1] << 16);
+                    lo2[m] = lb[0] | (lb[1] << 16);
+                }
+                qd[4 * k + 0] = hi2[0];
+                qd[4 * k + 1] = hi2[1];
+                qd[4 * k + 2] = lo2[0];
+                qd[4 * k + 3] = lo2[1];
+            }
+        }
+        cur_b = TB;
+    } else if constexpr (TB != 0) {
         load_query<D, G>(reinterpret_cast<const uint4 *>(uqw + jq * (D * G / 8)), u);
         cur_b = TB;
     } else {
 #pragma unroll
         for (int i = 0; i < D * G / 8; ++i) u[i] = 0u;
     }
-    // this lane's head in the softmax: j % G
-    const float sq = sq_lds[(lane & 3) % G];
+    // this lane's head in the softmax: j % G (dense keys: the plain scale)
+    const float sq = TB == kDenseTB ? A.scale * 1.4426950408889634f : sq_lds[(lane & 3) % G];
     float *pb = pbuf[wave];
 
     auto ensure_query = [&](int b) {
@@ -931,7 +1055,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             constexpr int SC = decltype(cur)::value;
 #pragma unroll
             for (int i = 0; i < kBufs; ++i) {
-                if (dd[i].live) compute_page<D, G, TB, DBG>(A, dd[i], R[i], len, head0, u, sq, lut, rlev, pb, st, acc);
+                if (dd[i].live) compute_page<D, G, TB, DBG>(A, dd[i], R[i], len, head0, u, qd, sq, lut, rlev, pb, st, acc);
                 if (refill && i == 0) {
                     if (SC == 0) e_ph0 = bt_raw(refill_c0);
                     else e_ph1 = bt_raw(refill_c0);
@@ -968,7 +1092,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             for (int i = 0; i < kBufs; ++i) {
                 if (k + i < nvalid) {
                     ensure_query(dd[i].b);
-                    compute_page<D, G, TB, DBG>(A, dd[i], R[i], len, head0, u, sq, lut, rlev, pb, st, acc);
+                    compute_page<D, G, TB, DBG>(A, dd[i], R[i], len, head0, u, qd, sq, lut, rlev, pb, st, acc);
                 }
                 dd[i] = desc(min(k + i + kBufs, last));
                 load_page<D, TB>(A, dd[i], kvh, R[i]);
@@ -1075,13 +1199,105 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     if (tid == 0) __hip_atomic_store(&A.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- decompress (the first step of decompress-then-dot, the path the codes
+// avoid): the dense key r~ * u(centres(c)) of every (token, KV head) of the
+// resident pages, rounded to bf16 and written token-major to the dense key
+// pool.  One wave per (sequence, page, KV head); lane (t, j) decodes the d/4
+// components of slice j of token t as the coded kernels do and stores them
+// as 2*(d/4) contiguous bytes. ----
+template <int D, int B>
+__device__ __forceinline__ void decompress_slice(const uint32_t (&cw)[8], const float2 *__restrict__ lut, float rr,
+                                                 uint16_t *dst) {
+    constexpr int NA = D / 4;
+    const int j = threadIdx.x & 3;
+    const uint32_t az_base = 8u * ((j == 3) ? lut_azimuth(B) : lut_polar(B));
+    const uint32_t pad_base = 8u * ((j == 3) ? kLutOnes : lut_polar(B));
+    const char *lutb = reinterpret_cast<const char *>(lut);
+    CodeAddr<B> ca;
+    ca.init(cw);
+    float w[NA];
+    float P = 1.f;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const uint32_t c8 = ca.at(cw, i);
+        uint32_t e8;
+        if (i == NA - 2) e8 = az_base + c8;
+        else if (i == NA - 1) e8 = pad_base + c8;
+        else e8 = 8u * lut_polar(B) + c8;
+        const float2 cs = *reinterpret_cast<const float2 *>(lutb + e8);
+        w[i] = P * cs.x;
+        P = P * cs.y;
+    }
+    const float sc = rr * slice_prefix(P, j);
+    uint32_t pk[NA / 2];
+#pragma unroll
+    for (int i = 0; i < NA / 2; ++i) pk[i] = bf16_rne(sc * w[2 * i]) | (bf16_rne(sc * w[2 * i + 1]) << 16);
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int i = 0; i < NA / 8; ++i) d4[i] = make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_decompress(DecodeArgs A) {
+    __shared__ float2 lut[kLutEntries];
+    for (int e = threadIdx.x; e < kLutEntries; e += 256) lut[e] = A.lut[e];
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int kvh = blockIdx.x * 4 + wave, p = blockIdx.y, seq = blockIdx.z;
+    if (kvh >= A.hkv) return;
+    const int len = max(0, min(A.seq_lens[seq], A.max_pages * kPage));
+    if (p >= (len + kPage - 1) / kPage) return;
+    const int ph = A.block_table[(int64_t)seq * A.max_pages + p];
+    if (ph < 0 || (int64_t)ph >= A.num_pages) {
+        if (lane == 0) atomicOr(A.err, 2u);
+        return;
+    }
+    const int b = A.page_bits[ph];
+    if (b < 2 || b > 8 || !((A.tier_mask >> b) & 1u) || !((kSupportedTiers >> b) & 1u)) {
+        if (lane == 0) atomicOr(A.err, 4u);
+        return;
+    }
+    const uint64_t off = A.page_off ? A.page_off[ph] : (uint64_t)ph * (uint64_t)A.page_stride;
+    // the lane's code slice (32 bytes from its start, as the mixed-tier loads)
+    const int t = lane >> 2, j = lane & 3;
+    const int KB = record_bytes(D, b);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + off + (uint64_t)kvh * kPage * KB, kPage * KB);
+    uint32_t cw[8];
+    const int vo = t * KB + j * (KB / 4);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 16 * k, 0, 0);
+        cw[4 * k + 0] = x[0]; cw[4 * k + 1] = x[1]; cw[4 * k + 2] = x[2]; cw[4 * k + 3] = x[3];
+    }
+    const int64_t pk = (int64_t)ph * A.hkv + kvh;
+    const float rr = A.rlev[kvh * 256 + A.rcode[pk * kPage + t]];
+    uint16_t *dst = A.kdense + (pk * kPage + t) * D + j * (D / 4);
+    switch (b) {
+        case 2: decompress_slice<D, 2>(cw, lut, rr, dst); break;
+        case 3: decompress_slice<D, 3>(cw, lut, rr, dst); break;
+        case 4: decompress_slice<D, 4>(cw, lut, rr, dst); break;
+        case 6: decompress_slice<D, 6>(cw, lut, rr, dst); break;
+        default: decompress_slice<D, 8>(cw, lut, rr, dst); break;
+    }
+}
+
+hipError_t launch_decompress(const DecodeArgs &a, int d, int B, hipStream_t s) {
+    if (B == 0) return hipSuccess;
+    const dim3 grid((unsigned)((a.hkv + 3) / 4), (unsigned)a.max_pages, (unsigned)B);
+    if (d == 128) hipLaunchKernelGGL(k_decompress<128>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_decompress<64>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int D, int G>
 static void launch_dg(const DecodeArgs &a, int tb, dim3 grid, hipStream_t s) {
     if (a.logits) {  // debug variant: stores the logits; generic tier dispatch
-        hipLaunchKernelGGL((k_decode<D, G, 0, true>), grid, dim3(kThreads), 0, s, a);
+        if (tb == kDenseTB) hipLaunchKernelGGL((k_decode<D, G, kDenseTB, true>), grid, dim3(kThreads), 0, s, a);
+        else hipLaunchKernelGGL((k_decode<D, G, 0, true>), grid, dim3(kThreads), 0, s, a);
         return;
     }
     switch (tb) {
+        case kDenseTB: hipLaunchKernelGGL((k_decode<D, G, kDenseTB, false>), grid, dim3(kThreads), 0, s, a); break;
         case 2: hipLaunchKernelGGL((k_decode<D, G, 2, false>), grid, dim3(kThreads), 0, s, a); break;
         case 3: hipLaunchKernelGGL((k_decode<D, G, 3, false>), grid, dim3(kThreads), 0, s, a); break;
         case 4: hipLaunchKernelGGL((k_decode<D, G, 4, false>), grid, dim3(kThreads), 0, s, a); break;
@@ -1097,6 +1313,7 @@ hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s
     int tb = 0;
     // single-tier pools at a fixed page stride take the tier-specialised kernel
     if (__builtin_popcount(a.tier_mask) == 1 && !a.page_off) tb = __builtin_ctz(a.tier_mask);
+    if (a.dense) tb = kDenseTB;
     if (d == 128) {
         if (G == 4) launch_dg<128, 4>(a, tb, grid, s);
         else if (G == 2) launch_dg<128, 2>(a, tb, grid, s);

@@ -351,9 +351,13 @@ ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool, const f
     return SKA_OK;
 }
 
-ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num_q_heads,
-                                const int32_t *block_table, int max_pages, const int32_t *seq_lens,
-                                float scale, int num_splits, float *out, float *logits_dbg, void *stream) {
+namespace {
+
+// One decode call: ADA over the cache's coded pools (k_dense NULL) or, for
+// the dense baseline, over bf16 keys k_dense with the cache's values.
+ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, int batch, int num_q_heads,
+                       const int32_t *block_table, int max_pages, const int32_t *seq_lens,
+                       float scale, int num_splits, float *out, float *logits_dbg, void *stream) {
     if (!c) return SKA_ERR_INVALID;
     if (batch < 0 || num_q_heads < 1 || max_pages < 1 || num_splits < 0) return SKA_ERR_INVALID;
     if (!std::isfinite(scale) || scale < 0.f) return SKA_ERR_INVALID;
@@ -422,6 +426,8 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     da.part_ml = (float *)(ws + off_pm);
     da.logits = logits_dbg;
     da.out = out;
+    da.kdense = const_cast<uint16_t *>(k_dense);
+    da.dense = k_dense != nullptr;
     da.counters = c->d_cnt;
     da.err = c->d_err;
     da.num_pages = c->pool.num_pages;
@@ -437,6 +443,50 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
     if (launch_decode(da, d, G, batch, s) != hipSuccess) return SKA_ERR_HIP;
     if (ev && hipEventRecord(ev[1], s) != hipSuccess) return SKA_ERR_HIP;
 
+    return SKA_OK;
+}
+
+}  // namespace
+
+ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num_q_heads,
+                                const int32_t *block_table, int max_pages, const int32_t *seq_lens,
+                                float scale, int num_splits, float *out, float *logits_dbg, void *stream) {
+    return decode_impl(c, nullptr, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale, num_splits,
+                       out, logits_dbg, stream);
+}
+
+ska_status ska_dense_decode_attention(ska_cache *c, const uint16_t *k_dense, const float *q, int batch,
+                                      int num_q_heads, const int32_t *block_table, int max_pages,
+                                      const int32_t *seq_lens, float scale, int num_splits, float *out,
+                                      float *logits_dbg, void *stream) {
+    if (!k_dense) return SKA_ERR_INVALID;
+    return decode_impl(c, k_dense, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale, num_splits,
+                       out, logits_dbg, stream);
+}
+
+ska_status ska_decompress_keys(ska_cache *c, const int32_t *block_table, int batch, int max_pages,
+                               const int32_t *seq_lens, uint16_t *k_dense, void *stream) {
+    if (!c || batch < 0 || max_pages < 1) return SKA_ERR_INVALID;
+    if (batch == 0) return SKA_OK;
+    if (!block_table || !seq_lens || !k_dense) return SKA_ERR_INVALID;
+    if (batch > 65535 || max_pages > 65535) return SKA_ERR_UNSUPPORTED;
+    DecodeArgs da{};
+    da.kcode = c->pool.kcode;
+    da.page_off = c->pool.page_off;
+    da.rcode = c->pool.rcode;
+    da.page_bits = c->pool.page_bits;
+    da.block_table = block_table;
+    da.seq_lens = seq_lens;
+    da.lut = c->d_lut;
+    da.rlev = c->d_rlev;
+    da.kdense = k_dense;
+    da.err = c->d_err;
+    da.num_pages = c->pool.num_pages;
+    da.page_stride = c->page_stride;
+    da.hkv = c->pool.num_kv_heads;
+    da.max_pages = max_pages;
+    da.tier_mask = c->pool.tier_mask;
+    if (launch_decompress(da, c->pool.d, batch, (hipStream_t)stream) != hipSuccess) return SKA_ERR_HIP;
     return SKA_OK;
 }
 

@@ -95,6 +95,8 @@ struct DecodeArgs {
     float *part_ml;          // [B][hq][nsplit][2]
     float *logits;           // debug [B][hq][max_pages*16] or NULL
     float *out;              // [B][hq][d]
+    uint16_t *kdense;        // dense bf16 keys [num_pages][hkv][16][d] (dense decode: read; decompress: written)
+    int dense;               // dense decode: keys from kdense, no codes
     uint32_t *counters;      // [B][hkv] finished workgroups per group, zero between calls
     uint32_t *err;
     int64_t num_pages;
@@ -115,6 +117,7 @@ hipError_t launch_calibrate(const float *keys, int64_t n, int hkv, int d, unsign
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t *p, int64_t n, hipStream_t s);
+hipError_t launch_decompress(const DecodeArgs &a, int d, int B, hipStream_t s);
 // decode workgroups resident per CU (two waves per SIMD in all)
 int decode_workgroups_per_cu();
 

@@ -22,8 +22,9 @@ Q_CODED, Q_EXACT = 0, 1
 PAGE = 16
 DEVERR_SLOT, DEVERR_PAGE, DEVERR_TIER = 1, 2, 4
 
-SYMBOLS = ("ska_encode_keys", "ska_decode_attention", "ska_get_radius_range", "ska_device_errors",
-           "ska_profile_begin", "ska_profile_read", "ska_free", "ska_status_string")
+SYMBOLS = ("ska_encode_keys", "ska_decode_attention", "ska_dense_decode_attention", "ska_decompress_keys",
+           "ska_get_radius_range", "ska_device_errors", "ska_profile_begin", "ska_profile_read", "ska_free",
+           "ska_status_string")
 
 
 class SkaError(RuntimeError):
@@ -64,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.ska_encode_keys.argtypes = [ctypes.POINTER(P), ctypes.POINTER(PoolDesc), P, P, P, i64, P, P]
         L.ska_decode_attention.restype = i
         L.ska_decode_attention.argtypes = [P, P, i, i, P, i, P, f, i, P, P, P]
+        L.ska_dense_decode_attention.restype = i
+        L.ska_dense_decode_attention.argtypes = [P, P, P, i, i, P, i, P, f, i, P, P, P]
+        L.ska_decompress_keys.restype = i
+        L.ska_decompress_keys.argtypes = [P, P, i, i, P, P, P]
         L.ska_get_radius_range.restype = i
         L.ska_get_radius_range.argtypes = [P, P]
         L.ska_device_errors.restype = i
@@ -181,6 +186,31 @@ def decode_attention(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, s
                                    _stream(stream))
     _check(s, "ska_decode_attention")
     return out
+
+
+def dense_decode_attention(cache: Cache, k_dense: torch.Tensor, q: torch.Tensor, block_table: torch.Tensor,
+                           seq_lens: torch.Tensor, scale: float = 0.0, num_splits: int = 0,
+                           out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """ska_dense_decode_attention: keys bf16 bits k_dense [num_pages][hkv][16][d] (int16/uint16 view),
+    the cache's values; otherwise as decode_attention."""
+    B, hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    s = lib().ska_dense_decode_attention(cache.handle, _ptr(k_dense), _ptr(q), B, hq, _ptr(block_table),
+                                         int(block_table.shape[1]), _ptr(seq_lens), float(scale), int(num_splits),
+                                         _ptr(out), _ptr(logits), _stream(stream))
+    _check(s, "ska_dense_decode_attention")
+    return out
+
+
+def decompress_keys(cache: Cache, block_table: torch.Tensor, seq_lens: torch.Tensor, k_dense: torch.Tensor,
+                    stream=None) -> torch.Tensor:
+    """ska_decompress_keys: writes bf16 r~ u(c) of the resident pages into k_dense [num_pages][hkv][16][d]."""
+    s = lib().ska_decompress_keys(cache.handle, _ptr(block_table), int(block_table.shape[0]),
+                                  int(block_table.shape[1]), _ptr(seq_lens), _ptr(k_dense), _stream(stream))
+    _check(s, "ska_decompress_keys")
+    return k_dense
 
 
 def radius_range(cache: Cache) -> np.ndarray:

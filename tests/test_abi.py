@@ -91,3 +91,9 @@ def test_null_free_and_queries():
     assert L.ska_get_radius_range(None, None) == ska.SKA_ERR_INVALID
     v = ctypes.c_uint32()
     assert L.ska_device_errors(None, None, ctypes.byref(v)) == ska.SKA_ERR_INVALID
+
+
+def test_baseline_entry_points_reject_bad_arguments_without_a_cache():
+    L = ska.lib()
+    assert L.ska_dense_decode_attention(None, 16, 16, 1, 32, 16, 4, 16, 0.0, 0, 16, None, None) == ska.SKA_ERR_INVALID
+    assert L.ska_decompress_keys(None, 16, 1, 4, 16, 16, None) == ska.SKA_ERR_INVALID
