@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--copies", type=int, default=2, help="pool copies alternated across steps")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the dense-bf16 and decompress-then-dot timings on the same pages")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle timing")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain copy kernel of this many MiB (counter calibration)")
@@ -140,7 +142,15 @@ def main():
         ska.encode_keys(cache, keys, vals, slot, radius_range=rng)
         rng = ska.radius_range(cache)
         caches.append(cache)
-    del keys, vals, slot
+    del vals
+    # dense bf16 key pools for the baselines (token-major [num_pages][hkv][16][d]), one per pool copy
+    kdense = []
+    if not args.no_baselines:
+        for c in range(args.copies):
+            kd = torch.zeros((w.num_pages, w.hkv, 16, w.d), dtype=torch.bfloat16, device=dev)
+            kd[slot // 16, :, slot % 16, :] = keys.to(torch.bfloat16)
+            kdense.append(kd.view(torch.int16))
+    del keys, slot
     torch.cuda.synchronize()
     log("encoded %d pool copies (%.1fs)" % (args.copies, time.time() - t0))
     q = torch.from_numpy(w.q).to(dev)
@@ -202,6 +212,49 @@ def main():
             "kernel_us_p10_p50_p90": [round(float(np.percentile(prof, p)) * 1e3, 2) for p in (10, 50, 90)],
             "alg_bytes_per_launch": int(kb)}
 
+    baselines = None
+    if kdense:
+        # the same pages read by the two paths the codes are set against: dense
+        # bf16 keys, and decompress-then-dot (r~ u(c) written to a dense pool,
+        # then the dense decode); values, block table and query as above
+        def run_dense(i):
+            ska.dense_decode_attention(caches[i % nc], kdense[i % nc], q, bt, sl, num_splits=args.splits, out=out)
+
+        def run_dtd(i):
+            ska.decompress_keys(caches[i % nc], bt, sl, kdense[i % nc])
+            ska.dense_decode_attention(caches[i % nc], kdense[i % nc], q, bt, sl, num_splits=args.splits, out=out)
+
+        def timed_fn(fn, steps):
+            for i in range(min(args.warmup, 5)):
+                fn(i)
+            torch.cuda.synchronize()
+            ev0.record()
+            for i in range(steps):
+                fn(i)
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / steps
+
+        res_t = w.n_tokens * w.hkv                      # resident (token, KV head) units
+        pages_kv = sum((int(n) + 15) // 16 for n in w.seq_lens) * w.hkv
+        qo = w.B * w.hq * w.d * 4 * 2
+        dense_bytes = res_t * 4 * w.d + pages_kv * 4 + qo
+        # the decompress kernel reads the codes, radius bytes, block table and
+        # headers (the coded step's bytes without values, query and output)
+        code_bytes = step_bytes - qo - res_t * 2 * w.d
+        dtd_bytes = code_bytes + res_t * 2 * w.d + dense_bytes
+        ms_dense = float(timed_fn(run_dense, args.steps))
+        ms_dtd = float(timed_fn(run_dtd, args.steps))
+        log("baselines: dense bf16 %.2f us/step, decompress-then-dot %.2f us/step" % (ms_dense * 1e3, ms_dtd * 1e3))
+        baselines = {
+            "dense_bf16": {"us_per_step": round(ms_dense * 1e3, 2), "bytes_per_step": int(dense_bytes),
+                           "GB/s": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1)},
+            "decompress_then_dot": {"us_per_step": round(ms_dtd * 1e3, 2), "bytes_per_step": int(dtd_bytes),
+                                    "GB/s": round(dtd_bytes / (ms_dtd * 1e-3) / 1e9, 1)},
+            "ada_speedup": {"vs_dense_bf16": round(ms_dense / ms_per_step, 3),
+                            "vs_decompress_then_dot": round(ms_dtd / ms_per_step, 3)},
+        }
+
     cpu = None
     if args.cpu_seqs > 0:
         log("timing the CPU oracle on %d sequences" % args.cpu_seqs)
@@ -232,6 +285,7 @@ def main():
                    "values": "bf16", "pool_copies": nc, "splits": args.splits or "auto"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "baselines": baselines,
     }
     print(json.dumps(line), flush=True)
 

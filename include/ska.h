@@ -160,7 +160,7 @@ ska_status ska_dense_decode_attention(ska_cache *cache, const uint16_t *k_dense,
  * each row of the block table) and every KV head, into k_dense (layout as in
  * ska_dense_decode_attention; other pages are left untouched).  Pages whose
  * id or header is out of range are skipped and flagged (ska_device_errors).
- * batch and max_pages are at most 65535.  Returns SKA_OK. */
+ * batch is at most 65535 and max_pages at most 64 * 65535.  Returns SKA_OK. */
 ska_status ska_decompress_keys(ska_cache *cache, const int32_t *block_table, int batch, int max_pages,
                                const int32_t *seq_lens, uint16_t *k_dense, void *stream);
 

@@ -1237,55 +1237,80 @@ __device__ __forceinline__ void decompress_slice(const uint32_t (&cw)[8], const 
     for (int i = 0; i < NA / 8; ++i) d4[i] = make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);
 }
 
+constexpr int kDecompChunk = 64;   // pages per decompress workgroup
+
 template <int D>
-__global__ __launch_bounds__(256) void k_decompress(DecodeArgs A) {
+__global__ __launch_bounds__(kThreads) void k_decompress(DecodeArgs A) {
+    // one workgroup per (KV head, sequence, chunk of kDecompChunk pages);
+    // wave w takes pages w, w + kWaves, ... of the chunk, requesting the next
+    // page's codes before decoding the current one
     __shared__ float2 lut[kLutEntries];
-    for (int e = threadIdx.x; e < kLutEntries; e += 256) lut[e] = A.lut[e];
+    for (int e = threadIdx.x; e < kLutEntries; e += kThreads) lut[e] = A.lut[e];
     __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int kvh = blockIdx.x * 4 + wave, p = blockIdx.y, seq = blockIdx.z;
-    if (kvh >= A.hkv) return;
-    const int len = max(0, min(A.seq_lens[seq], A.max_pages * kPage));
-    if (p >= (len + kPage - 1) / kPage) return;
-    const int ph = A.block_table[(int64_t)seq * A.max_pages + p];
-    if (ph < 0 || (int64_t)ph >= A.num_pages) {
-        if (lane == 0) atomicOr(A.err, 2u);
-        return;
-    }
-    const int b = A.page_bits[ph];
-    if (b < 2 || b > 8 || !((A.tier_mask >> b) & 1u) || !((kSupportedTiers >> b) & 1u)) {
-        if (lane == 0) atomicOr(A.err, 4u);
-        return;
-    }
-    const uint64_t off = A.page_off ? A.page_off[ph] : (uint64_t)ph * (uint64_t)A.page_stride;
-    // the lane's code slice (32 bytes from its start, as the mixed-tier loads)
+    const int kvh = blockIdx.x, seq = blockIdx.y;
     const int t = lane >> 2, j = lane & 3;
-    const int KB = record_bytes(D, b);
-    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + off + (uint64_t)kvh * kPage * KB, kPage * KB);
-    uint32_t cw[8];
-    const int vo = t * KB + j * (KB / 4);
+    const int len = max(0, min(A.seq_lens[seq], A.max_pages * kPage));
+    const int npages = (len + kPage - 1) / kPage;
+    const int p_end = min(npages, (int)(blockIdx.z + 1) * kDecompChunk);
+    struct Pg {
+        int ph, b;
+        uint32_t cw[8];
+        uint32_t rc;
+    };
+    // header, codes and radius byte of page p (ph < 0: nothing to do)
+    auto fetch = [&](int p, Pg &g) {
+        g.ph = -1;
+        g.b = 0;
+        if (p >= p_end) return;
+        const int ph = A.block_table[(int64_t)seq * A.max_pages + p];
+        if (ph < 0 || (int64_t)ph >= A.num_pages) {
+            if (lane == 0) atomicOr(A.err, 2u);
+            return;
+        }
+        const int b = A.page_bits[ph];
+        if (b < 2 || b > 8 || !((A.tier_mask >> b) & 1u) || !((kSupportedTiers >> b) & 1u)) {
+            if (lane == 0) atomicOr(A.err, 4u);
+            return;
+        }
+        const uint64_t off = A.page_off ? A.page_off[ph] : (uint64_t)ph * (uint64_t)A.page_stride;
+        const int KB = record_bytes(D, b);
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + off + (uint64_t)kvh * kPage * KB, kPage * KB);
+        const int vo = t * KB + j * (KB / 4);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 16 * k, 0, 0);
-        cw[4 * k + 0] = x[0]; cw[4 * k + 1] = x[1]; cw[4 * k + 2] = x[2]; cw[4 * k + 3] = x[3];
-    }
-    const int64_t pk = (int64_t)ph * A.hkv + kvh;
-    const float rr = A.rlev[kvh * 256 + A.rcode[pk * kPage + t]];
-    uint16_t *dst = A.kdense + (pk * kPage + t) * D + j * (D / 4);
-    switch (b) {
-        case 2: decompress_slice<D, 2>(cw, lut, rr, dst); break;
-        case 3: decompress_slice<D, 3>(cw, lut, rr, dst); break;
-        case 4: decompress_slice<D, 4>(cw, lut, rr, dst); break;
-        case 6: decompress_slice<D, 6>(cw, lut, rr, dst); break;
-        default: decompress_slice<D, 8>(cw, lut, rr, dst); break;
+        for (int k = 0; k < 2; ++k) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 16 * k, 0, 0);
+            g.cw[4 * k + 0] = x[0]; g.cw[4 * k + 1] = x[1]; g.cw[4 * k + 2] = x[2]; g.cw[4 * k + 3] = x[3];
+        }
+        g.rc = A.rcode[((int64_t)ph * A.hkv + kvh) * kPage + t];
+        g.ph = ph;
+        g.b = b;
+    };
+    Pg cur, nxt;
+    int p = blockIdx.z * kDecompChunk + wave;
+    fetch(p, cur);
+    for (; p < p_end; p += kWaves) {
+        fetch(p + kWaves, nxt);
+        if (cur.ph >= 0) {
+            const float rr = A.rlev[kvh * 256 + cur.rc];
+            uint16_t *dst = A.kdense + (((int64_t)cur.ph * A.hkv + kvh) * kPage + t) * D + j * (D / 4);
+            switch (cur.b) {
+                case 2: decompress_slice<D, 2>(cur.cw, lut, rr, dst); break;
+                case 3: decompress_slice<D, 3>(cur.cw, lut, rr, dst); break;
+                case 4: decompress_slice<D, 4>(cur.cw, lut, rr, dst); break;
+                case 6: decompress_slice<D, 6>(cur.cw, lut, rr, dst); break;
+                default: decompress_slice<D, 8>(cur.cw, lut, rr, dst); break;
+            }
+        }
+        cur = nxt;
     }
 }
 
 hipError_t launch_decompress(const DecodeArgs &a, int d, int B, hipStream_t s) {
     if (B == 0) return hipSuccess;
-    const dim3 grid((unsigned)((a.hkv + 3) / 4), (unsigned)a.max_pages, (unsigned)B);
-    if (d == 128) hipLaunchKernelGGL(k_decompress<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_decompress<64>, grid, dim3(256), 0, s, a);
+    const dim3 grid((unsigned)a.hkv, (unsigned)B, (unsigned)((a.max_pages + kDecompChunk - 1) / kDecompChunk));
+    if (d == 128) hipLaunchKernelGGL(k_decompress<128>, grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_decompress<64>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -469,7 +469,7 @@ ska_status ska_decompress_keys(ska_cache *c, const int32_t *block_table, int bat
     if (!c || batch < 0 || max_pages < 1) return SKA_ERR_INVALID;
     if (batch == 0) return SKA_OK;
     if (!block_table || !seq_lens || !k_dense) return SKA_ERR_INVALID;
-    if (batch > 65535 || max_pages > 65535) return SKA_ERR_UNSUPPORTED;
+    if (batch > 65535 || c->pool.num_kv_heads > 65535 || (max_pages + 63) / 64 > 65535) return SKA_ERR_UNSUPPORTED;
     DecodeArgs da{};
     da.kcode = c->pool.kcode;
     da.page_off = c->pool.page_off;
