@@ -102,6 +102,65 @@ def cpu_baseline(w, nseq: int, min_seconds: float):
                       (nseq, w.B, w.name, ntok, w.hq, reps)}
 
 
+def context_sweep(args, torch, ska, W):
+    """ADA and dense-bf16 decode steps at T = 8K, 32K and 128K with gqa_t32k's
+    batch shape (B=8, 32/8 heads, d=128, b=4, shuffled pages).  Keys and
+    values are drawn N(0,1) on the GPU (the times do not depend on their
+    values); two pool copies alternate as in the main measurement."""
+    dev = "cuda"
+    res = []
+    for T in (8192, 32768, 131072):
+        w = W.make("gqa_t32k", T / 32768.0, data=False)
+        g = torch.Generator(device=dev)
+        g.manual_seed(T)
+        slot = torch.from_numpy(w.slot).to(dev)
+        caches, kd, rng = [], [], None
+        for c in range(2):
+            keys = torch.randn((w.n_tokens, w.hkv, w.d), device=dev, generator=g)
+            vals = torch.randn((w.n_tokens, w.hkv, w.d), device=dev, generator=g).to(torch.bfloat16).view(torch.int16)
+            cache = ska.Cache(ska.DevicePools.for_workload(w, device=dev, poison=False))
+            ska.encode_keys(cache, keys, vals, slot, radius_range=rng)
+            rng = ska.radius_range(cache)
+            k = torch.zeros((w.num_pages, w.hkv, 16, w.d), dtype=torch.bfloat16, device=dev)
+            k[slot // 16, :, slot % 16, :] = keys.to(torch.bfloat16)
+            caches.append(cache)
+            kd.append(k.view(torch.int16))
+            del keys, vals
+        q = torch.randn((w.B, w.hq, w.d), device=dev, generator=g)
+        bt = torch.from_numpy(w.block_table).to(dev)
+        sl = torch.from_numpy(w.seq_lens).to(dev)
+        out = torch.empty((w.B, w.hq, w.d), dtype=torch.float32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def timed(fn, steps):
+            for i in range(5):
+                fn(i)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(steps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+
+        steps = max(20, args.steps // 2)
+        ms_ada = timed(lambda i: ska.decode_attention(caches[i % 2], q, bt, sl, out=out), steps)
+        ms_dense = timed(lambda i: ska.dense_decode_attention(caches[i % 2], kd[i % 2], q, bt, sl, out=out), steps)
+        ada_b = w.bytes_per_step()
+        res_t = w.n_tokens * w.hkv
+        dense_b = res_t * 4 * w.d + sum((int(n) + 15) // 16 for n in w.seq_lens) * w.hkv * 4 + w.B * w.hq * w.d * 8
+        res.append({"T": T, "ada_us": round(ms_ada * 1e3, 2), "ada_GB/s": round(ada_b / (ms_ada * 1e-3) / 1e9, 1),
+                    "dense_bf16_us": round(ms_dense * 1e3, 2),
+                    "dense_GB/s": round(dense_b / (ms_dense * 1e-3) / 1e9, 1),
+                    "ada_speedup": round(ms_dense / ms_ada, 3)})
+        log("context T=%d: ADA %.2f us, dense %.2f us (x%.2f)" % (T, ms_ada * 1e3, ms_dense * 1e3, ms_dense / ms_ada))
+        for c in caches:
+            c.free()
+        del caches, kd
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +170,8 @@ def main():
     ap.add_argument("--copies", type=int, default=2, help="pool copies alternated across steps")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--sweep-context", action="store_true",
+                    help="also time ADA and dense bf16 at T = 8K, 32K, 128K with gqa_t32k's batch shape")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the dense-bf16 and decompress-then-dot timings on the same pages")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle timing")
@@ -255,6 +316,12 @@ def main():
                             "vs_decompress_then_dot": round(ms_dtd / ms_per_step, 3)},
         }
 
+    sweep = None
+    if args.sweep_context:
+        del caches, kdense
+        torch.cuda.empty_cache()
+        sweep = context_sweep(args, torch, ska, W)
+
     cpu = None
     if args.cpu_seqs > 0:
         log("timing the CPU oracle on %d sequences" % args.cpu_seqs)
@@ -286,6 +353,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "baselines": baselines,
+        "context_sweep": sweep,
     }
     print(json.dumps(line), flush=True)
 
