@@ -78,6 +78,8 @@ def lib():
         L.ora_decoded_keys.argtypes = [i, i, i, P, P, P, i, P, P, P, i, P]
         L.ora_dense_decode.restype = i
         L.ora_dense_decode.argtypes = [i, i, P, P, P, i, i, P, i, P, d, P, P, i]
+        L.ora_rdr_plan.restype = i
+        L.ora_rdr_plan.argtypes = [i, P, P, P, i, P, P, P, i64, d, P, P, P, P, P, P]
         L.ora_max_threads.restype = i
         _lib = L
     return _lib
@@ -261,6 +263,30 @@ def dense_decode(k_dense, v, q, block_table, seq_lens, scale: float = 0.0, want_
     if r:
         raise ValueError("ora_dense_decode: bad argument")
     return (out, logits) if want_logits else out
+
+
+def rdr_plan(u, knorm, prot, tiers, eps, bytes_per_tier, budget: int, sigma: float):
+    """Rate-distortion retention plan for one sequence (see ora_rdr_plan).
+    Returns dict: tier [n] (0 = evicted), page [n], slot [n] (-1 evicted),
+    page_tier [npages], lambda, status (0 ok, 2 protected states over budget)."""
+    u = _c(u, np.float32)
+    knorm = _c(knorm, np.float32)
+    prot = _c(prot, np.uint8)
+    n = u.shape[0]
+    tiers = _c(tiers, np.int32)
+    eps = _c(eps, np.float64)
+    bpt = _c(bytes_per_tier, np.int64)
+    tier = np.zeros(n, np.uint8)
+    page = np.zeros(n, np.int32)
+    slot = np.zeros(n, np.int32)
+    pt = np.zeros(max(1, (n + PAGE - 1) // PAGE + len(tiers)), np.uint8)
+    npg = ctypes.c_int(0)
+    lam = ctypes.c_double(0.0)
+    r = lib().ora_rdr_plan(n, _p(u), _p(knorm), _p(prot), len(tiers), _p(tiers), _p(eps), _p(bpt), int(budget),
+                           float(sigma), _p(tier), _p(page), _p(slot), _p(pt), ctypes.byref(npg), ctypes.byref(lam))
+    if r == 1:
+        raise ValueError("ora_rdr_plan: bad argument")
+    return {"tier": tier, "page": page, "slot": slot, "page_tier": pt[: npg.value], "lambda": lam.value, "status": r}
 
 
 def max_threads() -> int:

@@ -651,6 +651,129 @@ int ora_dense_decode(int d, int hkv, const uint16_t *k_dense, const uint16_t *v,
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Rate-distortion retention (RDR) [SKV 2.2], one sequence: for every state
+ * (token) i choose residency z_i and tier b_i under a byte budget.
+ * Options: evict (0 bytes, distortion u_i: the state's utility is lost) or
+ * keep at tier k (bytes[k] bytes, distortion u_i * min(1, sigma*|k_i|*eps[k]):
+ * the logit error of ADA grows with the key's magnitude and the tier's angular
+ * error eps[k], sigma folding in the query magnitude and softmax scale).
+ * Protected states (prot[i] != 0) are kept at the widest tier.  The choice
+ * minimises sum D + lambda * sum bytes for a multiplier lambda found by 64
+ * bisection steps (the smallest lambda tried whose plan fits the budget):
+ * for each state, the option of least D + lambda*bytes, ties going to the
+ * earlier option in the order evict, tiers[0], ..., tiers[ntiers-1].
+ * Retained states are then packed into tier-homogeneous pages: tiers in the
+ * given (increasing) order, states in index order, 16 per page.
+ * Outputs: tier_out[i] (0 = evicted), page_out[i] / slot_out[i] (-1 when
+ * evicted), page_tier[p] for p < *npages, *lambda_out.  Returns 0, or 2 when
+ * the protected states alone exceed the budget (they are still kept, all
+ * others evicted), or 1 on a bad argument.  Arithmetic in binary64. */
+static int rdr_choose(double u, double kn, int ntiers, const double *eps, const int64_t *bytes, double sigma,
+                      double lambda, int prot)
+{
+    if (prot)
+        return ntiers;                       /* option index ntiers = widest tier */
+    int best = 0;                            /* 0: evict, k+1: tier k */
+    double bc = u;                           /* + lambda * 0 */
+    for (int k = 0; k < ntiers; ++k) {
+        double f = sigma * kn * eps[k];
+        if (f > 1.0)
+            f = 1.0;
+        double c = u * f + lambda * (double)bytes[k];
+        if (c < bc) {
+            bc = c;
+            best = k + 1;
+        }
+    }
+    return best;
+}
+
+int ora_rdr_plan(int n, const float *u, const float *knorm, const uint8_t *prot, int ntiers, const int *tiers,
+                 const double *eps, const int64_t *bytes, int64_t budget, double sigma,
+                 uint8_t *tier_out, int32_t *page_out, int32_t *slot_out, uint8_t *page_tier, int *npages,
+                 double *lambda_out)
+{
+    if (n < 0 || ntiers < 1 || ntiers > 8)
+        return 1;
+    for (int k = 1; k < ntiers; ++k)
+        if (tiers[k] <= tiers[k - 1] || bytes[k] < bytes[k - 1])
+            return 1;
+    /* bytes of a plan at multiplier lambda */
+#define RDR_TOTAL(lam, tot)                                                                        \
+    do {                                                                                           \
+        tot = 0;                                                                                   \
+        for (int i_ = 0; i_ < n; ++i_) {                                                           \
+            int o_ = rdr_choose(u[i_], knorm[i_], ntiers, eps, bytes, sigma, (lam), prot[i_] != 0); \
+            if (o_ > 0)                                                                            \
+                tot += bytes[o_ - 1];                                                              \
+        }                                                                                          \
+    } while (0)
+    /* a multiplier at which every unprotected state is evicted: above
+     * (u - D_k) / bytes_k for every state and tier */
+    double hi = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (prot[i])
+            continue;
+        for (int k = 0; k < ntiers; ++k) {
+            double f = sigma * (double)knorm[i] * eps[k];
+            if (f > 1.0)
+                f = 1.0;
+            double gain = (double)u[i] - (double)u[i] * f;
+            double r = gain / (double)bytes[k];
+            if (r > hi)
+                hi = r;
+        }
+    }
+    hi = 2.0 * hi + 1e-300;
+    double lo = 0.0, lambda;
+    int64_t tot;
+    int status = 0;
+    RDR_TOTAL(0.0, tot);
+    if (tot <= budget) {
+        lambda = 0.0;
+    } else {
+        RDR_TOTAL(hi, tot);
+        if (tot > budget)
+            status = 2;
+        for (int it = 0; it < 64; ++it) {
+            double mid = 0.5 * (lo + hi);
+            RDR_TOTAL(mid, tot);
+            if (tot <= budget)
+                hi = mid;
+            else
+                lo = mid;
+        }
+        lambda = hi;
+    }
+#undef RDR_TOTAL
+    /* the plan, then tier-homogeneous pages */
+    int page = 0;
+    for (int i = 0; i < n; ++i) {
+        int o = rdr_choose(u[i], knorm[i], ntiers, eps, bytes, sigma, lambda, prot[i] != 0);
+        tier_out[i] = (uint8_t)(o > 0 ? tiers[o - 1] : 0);
+        page_out[i] = -1;
+        slot_out[i] = -1;
+    }
+    for (int k = 0; k < ntiers; ++k) {
+        int cnt = 0;
+        for (int i = 0; i < n; ++i) {
+            if (tier_out[i] != tiers[k])
+                continue;
+            page_out[i] = page + cnt / ORA_PAGE;
+            slot_out[i] = cnt % ORA_PAGE;
+            ++cnt;
+        }
+        int np = (cnt + ORA_PAGE - 1) / ORA_PAGE;
+        for (int p = 0; p < np; ++p)
+            page_tier[page + p] = (uint8_t)tiers[k];
+        page += np;
+    }
+    *npages = page;
+    *lambda_out = lambda;
+    return status;
+}
+
 int ora_max_threads(void)
 {
 #ifdef _OPENMP
