@@ -164,6 +164,51 @@ ska_status ska_dense_decode_attention(ska_cache *cache, const uint16_t *k_dense,
 ska_status ska_decompress_keys(ska_cache *cache, const int32_t *block_table, int batch, int max_pages,
                                const int32_t *seq_lens, uint16_t *k_dense, void *stream);
 
+/* Rate-distortion retention parameters (section 2.2 of the page): the tier
+ * set B with, per tier, the angular error of f_b (the distortion surrogate:
+ * ADA's logit error grows with it, scaled by the query and key magnitudes)
+ * and the bytes one retained state occupies. */
+typedef struct {
+    int ntiers;           /* 1..8 */
+    int tiers[8];         /* increasing widths, each in 1..8 */
+    double eps[8];        /* angular error of each tier, >= 0 */
+    int64_t bytes[8];     /* bytes of one retained state at each tier, > 0, non-decreasing */
+    double sigma;         /* >= 0: query magnitude and softmax scale folded into the surrogate */
+} ska_rdr_params;
+
+/* ska_rdr_plan -- the RDR controller of section 2.2 of the page: for every
+ * state i (token) of each sequence, a residency and a tier under the
+ * sequence's byte budget, protected states kept at the widest tier, and the
+ * retained states grouped into tier-homogeneous pages for the decode
+ * kernel's header-guided streaming.
+ * Distortion surrogate (a reading; the page gives no formula): evicting i
+ * costs its utility u_i; keeping it at tier k costs
+ *     u_i * min(1, sigma * key_norm_i * eps_k).
+ * The plan takes, state by state, the option of least D + lambda * bytes
+ * (ties: evict, then the narrower tier) for the smallest multiplier lambda
+ * reached by 64 bisection steps whose plan fits the budget; by Everett's
+ * theorem no plan using no more bytes has a smaller total distortion.
+ * Retained states are packed tier by tier (tiers in increasing order),
+ * states in index order, 16 per page.  All arrays are device memory.
+ *   utility, key_norm  fp32 [batch][max_states];  protect uint8 [batch][max_states]
+ *   num_states int32 [batch] (states used in each row);  budget int64 [batch] bytes
+ *   tier_out   uint8 [batch][max_states]: 0 = evicted, else the tier's width
+ *   page_out, slot_out  int32 [batch][max_states]: page and slot of each
+ *              retained state, -1 when evicted
+ *   page_tier_out  uint8 [batch][max_pages_out]: width of each page;
+ *              max_pages_out >= ceil(max_states/16) + ntiers
+ *   npages_out int32 [batch], lambda_out double [batch],
+ *   status_out int32 [batch]: 0, or 2 when the protected states alone exceed
+ *              the budget (they are kept and every other state is evicted)
+ * Decisions are binary64 comparisons made as written (no contraction), so
+ * the plan is reproducible bit for bit.  Returns SKA_OK, SKA_ERR_INVALID on
+ * a bad parameter or size. */
+ska_status ska_rdr_plan(const ska_rdr_params *params, const float *utility, const float *key_norm,
+                        const uint8_t *protect, const int32_t *num_states, const int64_t *budget, int batch,
+                        int max_states, uint8_t *tier_out, int32_t *page_out, int32_t *slot_out,
+                        uint8_t *page_tier_out, int max_pages_out, int32_t *npages_out, double *lambda_out,
+                        int32_t *status_out, void *stream);
+
 /* The radius range in use (host [Hkv][2] = (R_lo, R_hi)). */
 ska_status ska_get_radius_range(const ska_cache *cache, double *range_out);
 

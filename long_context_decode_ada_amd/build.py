@@ -29,6 +29,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I" + os.path
 UNITS = {
     "k_decode.hip": [],
     "k_codes.hip": ["-ffp-contract=off"],
+    "k_rdr.hip": ["-ffp-contract=off"],
     "ska_api.cpp": ["-ffp-contract=off", "-fno-builtin"],
 }
 

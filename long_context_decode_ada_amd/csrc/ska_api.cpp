@@ -23,6 +23,7 @@
 
 #include "../../include/ska.h"
 #include "ska_internal.h"
+#include "ska_rdr.h"
 
 using namespace ska;
 
@@ -462,6 +463,50 @@ ska_status ska_dense_decode_attention(ska_cache *c, const uint16_t *k_dense, con
     if (!k_dense) return SKA_ERR_INVALID;
     return decode_impl(c, k_dense, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale, num_splits,
                        out, logits_dbg, stream);
+}
+
+ska_status ska_rdr_plan(const ska_rdr_params *p, const float *utility, const float *key_norm,
+                        const uint8_t *protect, const int32_t *num_states, const int64_t *budget, int batch,
+                        int max_states, uint8_t *tier_out, int32_t *page_out, int32_t *slot_out,
+                        uint8_t *page_tier_out, int max_pages_out, int32_t *npages_out, double *lambda_out,
+                        int32_t *status_out, void *stream) {
+    if (!p || batch < 0 || max_states < 0) return SKA_ERR_INVALID;
+    if (p->ntiers < 1 || p->ntiers > 8 || !(p->sigma >= 0.0) || !std::isfinite(p->sigma)) return SKA_ERR_INVALID;
+    for (int k = 0; k < p->ntiers; ++k) {
+        const int b = p->tiers[k];
+        if (b < 1 || b > 8 || !(p->eps[k] >= 0.0) || !std::isfinite(p->eps[k]) || p->bytes[k] <= 0)
+            return SKA_ERR_INVALID;
+        if (k > 0 && (b <= p->tiers[k - 1] || p->bytes[k] < p->bytes[k - 1])) return SKA_ERR_INVALID;
+    }
+    if (max_pages_out < (max_states + 15) / 16 + p->ntiers) return SKA_ERR_INVALID;
+    if (batch == 0) return SKA_OK;
+    if (!utility || !key_norm || !protect || !num_states || !budget || !tier_out || !page_out || !slot_out ||
+        !page_tier_out || !npages_out || !lambda_out || !status_out)
+        return SKA_ERR_INVALID;
+    RdrArgs a{};
+    a.u = utility;
+    a.knorm = key_norm;
+    a.prot = protect;
+    a.nstate = num_states;
+    a.budget = budget;
+    a.max_states = max_states;
+    a.ntiers = p->ntiers;
+    for (int k = 0; k < p->ntiers; ++k) {
+        a.tiers[k] = p->tiers[k];
+        a.eps[k] = p->eps[k];
+        a.bytes[k] = p->bytes[k];
+    }
+    a.sigma = p->sigma;
+    a.tier_out = tier_out;
+    a.page_out = page_out;
+    a.slot_out = slot_out;
+    a.page_tier = page_tier_out;
+    a.max_pages_out = max_pages_out;
+    a.npages = npages_out;
+    a.lambda = lambda_out;
+    a.status = status_out;
+    if (launch_rdr(a, batch, (hipStream_t)stream) != hipSuccess) return SKA_ERR_HIP;
+    return SKA_OK;
 }
 
 ska_status ska_decompress_keys(ska_cache *c, const int32_t *block_table, int batch, int max_pages,

@@ -23,8 +23,8 @@ PAGE = 16
 DEVERR_SLOT, DEVERR_PAGE, DEVERR_TIER = 1, 2, 4
 
 SYMBOLS = ("ska_encode_keys", "ska_decode_attention", "ska_dense_decode_attention", "ska_decompress_keys",
-           "ska_get_radius_range", "ska_device_errors", "ska_profile_begin", "ska_profile_read", "ska_free",
-           "ska_status_string")
+           "ska_rdr_plan", "ska_get_radius_range", "ska_device_errors", "ska_profile_begin", "ska_profile_read",
+           "ska_free", "ska_status_string")
 
 
 class SkaError(RuntimeError):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.ska_dense_decode_attention.argtypes = [P, P, P, i, i, P, i, P, f, i, P, P, P]
         L.ska_decompress_keys.restype = i
         L.ska_decompress_keys.argtypes = [P, P, i, i, P, P, P]
+        L.ska_rdr_plan.restype = i
+        L.ska_rdr_plan.argtypes = [ctypes.POINTER(RdrParams), P, P, P, P, P, i, i, P, P, P, P, i, P, P, P, P]
         L.ska_get_radius_range.restype = i
         L.ska_get_radius_range.argtypes = [P, P]
         L.ska_device_errors.restype = i
@@ -211,6 +213,39 @@ def decompress_keys(cache: Cache, block_table: torch.Tensor, seq_lens: torch.Ten
                                   int(block_table.shape[1]), _ptr(seq_lens), _ptr(k_dense), _stream(stream))
     _check(s, "ska_decompress_keys")
     return k_dense
+
+
+class RdrParams(ctypes.Structure):
+    _fields_ = [("ntiers", ctypes.c_int), ("tiers", ctypes.c_int * 8), ("eps", ctypes.c_double * 8),
+                ("bytes", ctypes.c_int64 * 8), ("sigma", ctypes.c_double)]
+
+
+def rdr_plan(utility: torch.Tensor, key_norm: torch.Tensor, protect: torch.Tensor, num_states: torch.Tensor,
+             budget: torch.Tensor, tiers, eps, bytes_per_tier, sigma: float, stream=None) -> dict:
+    """ska_rdr_plan on device tensors utility/key_norm fp32 [B][T], protect uint8 [B][T], num_states int32 [B],
+    budget int64 [B].  Returns dict of device tensors tier (uint8), page, slot (int32) [B][T],
+    page_tier (uint8) [B][P], npages (int32), lambda (float64), status (int32) [B]."""
+    B, T = utility.shape
+    p = RdrParams()
+    p.ntiers = len(tiers)
+    for k in range(len(tiers)):
+        p.tiers[k], p.eps[k], p.bytes[k] = int(tiers[k]), float(eps[k]), int(bytes_per_tier[k])
+    p.sigma = float(sigma)
+    dev = utility.device
+    P_out = (T + 15) // 16 + len(tiers)
+    o = {"tier": torch.zeros((B, T), dtype=torch.uint8, device=dev),
+         "page": torch.zeros((B, T), dtype=torch.int32, device=dev),
+         "slot": torch.zeros((B, T), dtype=torch.int32, device=dev),
+         "page_tier": torch.zeros((B, P_out), dtype=torch.uint8, device=dev),
+         "npages": torch.zeros(B, dtype=torch.int32, device=dev),
+         "lambda": torch.zeros(B, dtype=torch.float64, device=dev),
+         "status": torch.zeros(B, dtype=torch.int32, device=dev)}
+    s = lib().ska_rdr_plan(ctypes.byref(p), _ptr(utility), _ptr(key_norm), _ptr(protect), _ptr(num_states),
+                           _ptr(budget), B, T, _ptr(o["tier"]), _ptr(o["page"]), _ptr(o["slot"]),
+                           _ptr(o["page_tier"]), P_out, _ptr(o["npages"]), _ptr(o["lambda"]), _ptr(o["status"]),
+                           _stream(stream))
+    _check(s, "ska_rdr_plan")
+    return o
 
 
 def radius_range(cache: Cache) -> np.ndarray:

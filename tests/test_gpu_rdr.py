@@ -1,0 +1,159 @@
+"""GPU parity of the RDR controller (ska_rdr_plan) against the oracle's plan,
+bit for bit (tiers, pages, slots, page tiers, page counts, multipliers,
+status), and its use end to end: a plan turns a sequence into tier-homogeneous
+pages of retained tokens, which the coded decode then reads (section 2.2 of
+the page: RDR output feeds the header-guided decode)."""
+import math
+
+import numpy as np
+import pytest
+
+from long_context_decode_ada_amd import workloads as W
+from oracle import oracle as O
+from tests.parity_util import compare, gpu_run, oracle_run, say
+
+pytestmark = pytest.mark.gpu
+
+TIERS = [2, 4, 6, 8]
+EPS = [0.12, 0.031, 0.0078, 0.0019]
+D, HKV = 128, 8
+BYTES = [HKV * (16 * (((D - 1) * b + 127) // 128) + 1 + 2 * D) for b in TIERS]
+
+
+def _gpu_plan(u, kn, prot, n, budget, sigma):
+    import torch
+    from long_context_decode_ada_amd import ska
+    dev = "cuda"
+    r = ska.rdr_plan(torch.from_numpy(u).to(dev), torch.from_numpy(kn).to(dev), torch.from_numpy(prot).to(dev),
+                     torch.from_numpy(n).to(dev), torch.from_numpy(budget).to(dev), TIERS, EPS, BYTES, sigma)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in r.items()}
+
+
+def test_plan_matches_oracle_bit_for_bit():
+    rng = np.random.default_rng(21)
+    T = 40000
+    lens = np.array([0, 1, 17, 4999, 40000, 23456], np.int32)
+    B = len(lens)
+    u = rng.exponential(1.0, (B, T)).astype(np.float32)
+    u[:, ::7] *= 1e-3
+    kn = rng.uniform(3.0, 40.0, (B, T)).astype(np.float32)
+    prot = np.zeros((B, T), np.uint8)
+    prot[:, :4] = 1
+    for s in range(B):
+        prot[s, max(0, lens[s] - 64): lens[s]] = 1
+    fracs = [0.5, 0.3, 0.05, 0.35, 0.22, 1.1]
+    budget = np.array([int(f * n * BYTES[-1]) for f, n in zip(fracs, lens)], np.int64)
+    budget[2] = 3 * BYTES[-1]                           # 17 states, 17 protected: over budget
+    sigma = 0.04
+    g = _gpu_plan(u, kn, prot, lens, budget, sigma)
+    for s in range(B):
+        n = int(lens[s])
+        o = O.rdr_plan(u[s, :n], kn[s, :n], prot[s, :n], TIERS, EPS, BYTES, int(budget[s]), sigma)
+        say("[rdr] seq %d: n=%d status %d pages %d lambda %.6g" % (s, n, o["status"], len(o["page_tier"]), o["lambda"]))
+        assert g["status"][s] == o["status"]
+        assert g["npages"][s] == len(o["page_tier"])
+        assert g["lambda"][s] == o["lambda"]
+        assert np.array_equal(g["tier"][s, :n], o["tier"])
+        assert np.array_equal(g["page"][s, :n], o["page"])
+        assert np.array_equal(g["slot"][s, :n], o["slot"])
+        assert np.array_equal(g["page_tier"][s, : len(o["page_tier"])], o["page_tier"])
+
+
+def _planned_workload(seed):
+    """A gqa_t32k-shaped batch reduced by an RDR plan: per sequence, the
+    utility of a token is its attention mass under the batch's query (all
+    query heads), its key norm the mean over KV heads; the first 4 tokens and
+    the last 64 are protected; the budget is 30 % of the widest tier.  The
+    retained tokens become tier-homogeneous pages in a shared pool."""
+    w = W.make("gqa_t32k", 1 / 16, batch=3)               # T = 2048
+    rng = np.random.default_rng(seed)
+    g = w.hq // w.hkv
+    scale = 1.0 / math.sqrt(w.d)
+    keep_keys, keep_vals, plans = [], [], []
+    for s in range(w.B):
+        rows = W.token_keys(w, s)
+        k = w.keys[rows].astype(np.float64)                 # [n][hkv][d]
+        util = np.zeros(k.shape[0])
+        for h in range(w.hq):
+            lg = scale * (k[:, h // g, :] @ w.q[s, h].astype(np.float64))
+            p = np.exp(lg - lg.max())
+            util += p / p.sum()
+        kn = np.linalg.norm(k, axis=2).mean(1)
+        n = k.shape[0]
+        prot = np.zeros(n, np.uint8)
+        prot[:4] = 1
+        prot[-64:] = 1
+        plans.append((util.astype(np.float32), kn.astype(np.float32), prot, int(0.3 * n * BYTES[-1])))
+        keep_keys.append(w.keys[rows])
+        keep_vals.append(w.values[rows])
+    return w, plans, keep_keys, keep_vals, rng
+
+
+def test_rdr_plan_drives_the_coded_decode():
+    w, plans, keys_by_seq, vals_by_seq, rng = _planned_workload(22)
+    T = max(p[0].shape[0] for p in plans)
+    B = w.B
+    u = np.zeros((B, T), np.float32)
+    kn = np.zeros((B, T), np.float32)
+    prot = np.zeros((B, T), np.uint8)
+    lens = np.zeros(B, np.int32)
+    budget = np.zeros(B, np.int64)
+    for s, (ut, kt, pt, bt_) in enumerate(plans):
+        n = ut.shape[0]
+        u[s, :n], kn[s, :n], prot[s, :n], lens[s], budget[s] = ut, kt, pt, n, bt_
+    g = _gpu_plan(u, kn, prot, lens, budget, 0.05)
+    # pages of the plan -> physical pages of one shared pool
+    npg = g["npages"].astype(int)
+    total = int(npg.sum())
+    perm = rng.permutation(total)
+    max_pages = int(npg.max())
+    bt = np.zeros((B, max_pages), np.int32)
+    page_bits = np.zeros(total, np.uint8)
+    keys, vals, slots, kept_n = [], [], [], 0
+    k0 = 0
+    for s in range(B):
+        phys = perm[k0: k0 + npg[s]]
+        k0 += npg[s]
+        bt[s, : npg[s]] = phys
+        page_bits[phys] = g["page_tier"][s, : npg[s]]
+        n = int(lens[s])
+        kept = np.nonzero(g["tier"][s, :n])[0]
+        keys.append(keys_by_seq[s][kept])
+        vals.append(vals_by_seq[s][kept])
+        slots.append(phys[g["page"][s, kept]].astype(np.int64) * 16 + g["slot"][s, kept])
+        kept_n += len(kept)
+    # The decode maps token t of a row to slot t % 16 of page t / 16, so only
+    # a row's last page may be partly filled; the plan leaves one partial
+    # page per tier.  Each (sequence, tier) segment is therefore read as a
+    # row of its own (its pages in plan order, its tokens in slot order).
+    rows_bt, rows_len, rows_q = [], [], []
+    for s in range(B):
+        for t in TIERS:
+            pages = np.nonzero(g["page_tier"][s, : npg[s]] == t)[0]
+            if len(pages) == 0:
+                continue
+            n_t = int((g["tier"][s, : lens[s]] == t).sum())
+            row = np.zeros(max_pages, np.int32)
+            row[: len(pages)] = bt[s, pages]
+            rows_bt.append(row)
+            rows_len.append(n_t)
+            rows_q.append(w.q[s])
+    w2 = W.Workload(name="rdr", d=w.d, hq=w.hq, hkv=w.hkv, B=len(rows_bt), radius_mode=w.radius_mode,
+                    tier_mask=int(sum(1 << t for t in set(page_bits.tolist()))),
+                    seq_lens=np.array(rows_len, np.int32), block_table=np.stack(rows_bt), num_pages=total,
+                    page_bits=page_bits, page_off=None, bstride=8, kcode_bytes=0,
+                    keys=np.concatenate(keys), values=np.concatenate(vals), slot=np.concatenate(slots),
+                    q=np.stack(rows_q).astype(np.float32))
+    sizes = w2.hkv * 16 * np.array([O.kb(w2.d, int(b)) for b in page_bits], np.uint64)
+    w2.page_off = np.zeros(total, np.uint64)
+    w2.page_off[1:] = np.cumsum(sizes)[:-1]
+    w2.kcode_bytes = int(sizes.sum())
+    say("[rdr] %d sequences -> %d tier rows, %d pages, %d of %d tokens kept" %
+        (B, w2.B, total, kept_n, int(lens.sum())))
+    rng_r = O.calibrate(w2.keys)
+    gr = gpu_run(w2)
+    orr = oracle_run(w2, rng_r)
+    for k in ("kcode", "rcode", "v"):
+        assert np.array_equal(gr["pools"][k], orr["pools"][k]), k
+    compare(w2, gr, orr, rng_r, label="rdr pages")
