@@ -4,6 +4,7 @@ status), and its use end to end: a plan turns a sequence into tier-homogeneous
 pages of retained tokens, which the coded decode then reads (section 2.2 of
 the page: RDR output feeds the header-guided decode)."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -15,7 +16,16 @@ from tests.parity_util import compare, gpu_run, oracle_run, say
 pytestmark = pytest.mark.gpu
 
 TIERS = [2, 4, 6, 8]
-EPS = [0.12, 0.031, 0.0078, 0.0019]
+
+
+def _eps_table():
+    """eps(b) from tests/golden/rdr_eps_d128.txt (written by make_rdr_eps.py, oracle only)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rdr_eps_d128.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    return {int(b): float(e) for b, e in rows}
+
+
+EPS = [_eps_table()[b] for b in TIERS]
 D, HKV = 128, 8
 BYTES = [HKV * (16 * (((D - 1) * b + 127) // 128) + 1 + 2 * D) for b in TIERS]
 

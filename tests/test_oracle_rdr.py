@@ -11,13 +11,23 @@ behave as stated, zero-utility states go first, and the page packing is
 tier-homogeneous, dense and in state order.
 """
 import itertools
+import os
 
 import numpy as np
 
 from oracle import oracle as O
 
 TIERS = [2, 4, 6, 8]
-EPS = [0.12, 0.031, 0.0078, 0.0019]
+
+
+def _eps_table():
+    """eps(b) from tests/golden/rdr_eps_d128.txt (written by make_rdr_eps.py, oracle only)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rdr_eps_d128.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    return {int(b): float(e) for b, e in rows}
+
+
+EPS = [_eps_table()[b] for b in TIERS]
 D, HKV = 128, 8
 BYTES = [HKV * (16 * (((D - 1) * b + 127) // 128) + 1 + 2 * D) for b in TIERS]
 
@@ -43,8 +53,24 @@ def _inputs(seed, n):
     return u, kn
 
 
+def test_eps_table_is_what_its_generator_writes():
+    import importlib.util
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "make_rdr_eps.py")
+    spec = importlib.util.spec_from_file_location("make_rdr_eps", path)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    fresh = m.eps_table()
+    stored = _eps_table()
+    for b, e in fresh.items():
+        assert abs(stored[b] - e) <= 1e-6 * e
+    # the angular error roughly halves per bit
+    for b0, b1 in ((2, 3), (3, 4), (4, 6), (6, 8)):
+        ratio = stored[b0] / stored[b1]
+        assert 1.6 ** (b1 - b0) < ratio < 2.6 ** (b1 - b0)
+
+
 def test_lagrangian_plan_beats_every_plan_with_no_more_bytes():
-    tiers, eps = [2, 4, 8], [0.12, 0.031, 0.0019]
+    tiers, eps = [2, 4, 8], [EPS[0], EPS[1], EPS[3]]
     bpt = [BYTES[0], BYTES[1], BYTES[3]]
     for seed in range(6):
         n = 7
