@@ -26,11 +26,15 @@ constexpr int kRdrThreads = 1024;
 constexpr int kRdrWaves = kRdrThreads / 64;
 
 // 0: evict; k + 1: tier k (protected states: the widest tier)
+// (the tier loop runs over a fixed 8 with a guard, so that the parameters
+// are read at constant indices, once, into scalar registers)
 __device__ __forceinline__ int rdr_choose(double u, double kn, const RdrArgs &A, double lambda, bool prot) {
     if (prot) return A.ntiers;
     int best = 0;
     double bc = u;
-    for (int k = 0; k < A.ntiers; ++k) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (k >= A.ntiers) break;
         double f = A.sigma * kn * A.eps[k];
         if (f > 1.0) f = 1.0;
         const double c = u * f + lambda * (double)A.bytes[k];
@@ -81,8 +85,10 @@ __global__ __launch_bounds__(kRdrThreads) void k_rdr(RdrArgs A) {
     const int seq = blockIdx.x, tid = threadIdx.x;
     const int n = max(0, min(A.nstate[seq], A.max_states));
     const int64_t base = (int64_t)seq * A.max_states;
-    // each thread takes a contiguous run of states, so that runs in thread
-    // order are the states in index order
+    // the passes that only sum or take a maximum stride over the states
+    // (adjacent threads, adjacent states); the packing gives each thread a
+    // contiguous run, so that runs in thread order are the states in index
+    // order
     const int per = (n + kRdrThreads - 1) / kRdrThreads;
     const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
     const float *u = A.u + base;
@@ -91,9 +97,11 @@ __global__ __launch_bounds__(kRdrThreads) void k_rdr(RdrArgs A) {
 
     // a multiplier at which every unprotected state is evicted
     double hl = 0.0;
-    for (int i = i0; i < i1; ++i) {
+    for (int i = tid; i < n; i += kRdrThreads) {
         if (prot[i]) continue;
-        for (int k = 0; k < A.ntiers; ++k) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (k >= A.ntiers) break;
             double f = A.sigma * (double)kn[i] * A.eps[k];
             if (f > 1.0) f = 1.0;
             const double gain = (double)u[i] - (double)u[i] * f;
@@ -105,9 +113,24 @@ __global__ __launch_bounds__(kRdrThreads) void k_rdr(RdrArgs A) {
     hi = 2.0 * hi + 1e-300;
     auto total = [&](double lam) -> long long {
         long long t = 0;
-        for (int i = i0; i < i1; ++i) {
-            const int o = rdr_choose((double)u[i], (double)kn[i], A, lam, prot[i] != 0);
-            if (o > 0) t += A.bytes[o - 1];
+        // kB states per thread per round: their loads go out together
+        constexpr int kB = 8;
+        for (int i0s = tid; i0s < n; i0s += kB * kRdrThreads) {
+            float uu[kB], kk[kB];
+            uint8_t pp[kB];
+#pragma unroll
+            for (int e = 0; e < kB; ++e) {
+                const int i = min(i0s + e * kRdrThreads, n - 1);
+                uu[e] = u[i];
+                kk[e] = kn[i];
+                pp[e] = prot[i];
+            }
+#pragma unroll
+            for (int e = 0; e < kB; ++e) {
+                if (i0s + e * kRdrThreads >= n) break;
+                const int o = rdr_choose((double)uu[e], (double)kk[e], A, lam, pp[e] != 0);
+                if (o > 0) t += A.bytes[o - 1];
+            }
         }
         return block_reduce(t, [](long long a, long long b) { return a + b; }, redl);
     };
@@ -129,7 +152,7 @@ __global__ __launch_bounds__(kRdrThreads) void k_rdr(RdrArgs A) {
 
     // the plan, then tier-homogeneous pages: tiers in order, states in
     // index order, 16 per page
-    for (int i = i0; i < i1; ++i) {
+    for (int i = tid; i < n; i += kRdrThreads) {
         const int o = rdr_choose((double)u[i], (double)kn[i], A, lambda, prot[i] != 0);
         A.tier_out[base + i] = (uint8_t)(o > 0 ? A.tiers[o - 1] : 0);
         A.page_out[base + i] = -1;
