@@ -254,6 +254,14 @@ struct PageDesc {
     bool live;      // false: the loads go through empty descriptors and read nothing
 };
 
+// A wave-uniform address, read back into scalar registers.
+__device__ __forceinline__ const void *scalar_ptr(const void *p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
+}
+
 // Raw buffer descriptor (V#) over `bytes` bytes at a wave-uniform address:
 // loads past the end return 0 instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
@@ -1206,8 +1214,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 // components of slice j of token t as the coded kernels do and stores them
 // as 2*(d/4) contiguous bytes. ----
 template <int D, int B>
-__device__ __forceinline__ void decompress_slice(const uint32_t (&cw)[8], const float2 *__restrict__ lut, float rr,
-                                                 uint16_t *dst) {
+__device__ __forceinline__ void decompress_pack(const uint32_t (&cw)[8], const float2 *__restrict__ lut, float rr,
+                                                uint32_t (&pk)[D / 8]) {
     constexpr int NA = D / 4;
     const int j = threadIdx.x & 3;
     const uint32_t az_base = 8u * ((j == 3) ? lut_azimuth(B) : lut_polar(B));
@@ -1229,88 +1237,219 @@ __device__ __forceinline__ void decompress_slice(const uint32_t (&cw)[8], const 
         P = P * cs.y;
     }
     const float sc = rr * slice_prefix(P, j);
-    uint32_t pk[NA / 2];
+    // gfx950 converts a pair of binary32 values to bf16 (round to nearest
+    // even) in one instruction
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int i = 0; i < NA / 2; ++i) pk[i] = bf16_rne(sc * w[2 * i]) | (bf16_rne(sc * w[2 * i + 1]) << 16);
-    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
-#pragma unroll
-    for (int i = 0; i < NA / 8; ++i) d4[i] = make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);
+    for (int i = 0; i < NA / 2; ++i) {
+        const f32x2 v = {sc * w[2 * i], sc * w[2 * i + 1]};
+        pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    }
 }
 
 constexpr int kDecompChunk = 64;   // pages per decompress workgroup
 
-template <int D>
+// Decompression of the keys to a dense bf16 pool [num_pages][hkv][16][D]:
+// one workgroup per (KV head, sequence, chunk of kDecompChunk pages), wave w
+// taking pages w, w + kWaves, ... of the chunk.  TB is the tier of a pool of
+// one tier at a fixed stride; TB = 0 reads the tier of each page from its
+// header (and its offset from the page offsets when the pool has them).
+//
+// The block-table entries of a wave's pages (and for TB = 0 their headers
+// and offsets) are read once, one page per lane, and the radius levels of
+// the head sit in LDS, so inside the loop the only global accesses are the
+// page loads and the stores.  Every page slot issues the same loads and
+// stores whether or not it holds a page: a slot past the chunk, a bad page id
+// or a bad header gets an empty descriptor (its loads read zeros, its stores
+// are dropped), and errors are gathered in a register and posted once at the
+// end.  With the memory operations the same on every path the compiler's
+// wait before decoding a page counts exactly that page's loads, not the
+// stores of the page before.
+//
+// The dense block of a (page, head) leaves through LDS so that each store
+// covers one contiguous 1 KB run, and the stores are marked non-temporal:
+// the dense pool streams out to HBM rather than displacing cached lines.
+template <int D, int TB>
 __global__ __launch_bounds__(kThreads) void k_decompress(DecodeArgs A) {
-    // one workgroup per (KV head, sequence, chunk of kDecompChunk pages);
-    // wave w takes pages w, w + kWaves, ... of the chunk, requesting the next
-    // page's codes before decoding the current one
+    constexpr int kPer = kDecompChunk / kWaves;
+    static_assert(kDecompChunk % kWaves == 0 && kPer <= 64, "pages per wave");
+    constexpr int kOut = kPage * D * 2;                  // bytes of one (page, head) dense block
+    static_assert(kOut == (D / 32) * 64 * 16, "one store per lane and 1 KB run");
+    constexpr int kStoreNT = 2;                          // cache policy: non-temporal
     __shared__ float2 lut[kLutEntries];
-    for (int e = threadIdx.x; e < kLutEntries; e += kThreads) lut[e] = A.lut[e];
-    __syncthreads();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    __shared__ float rlev[256];
+    __shared__ uint4 stage[kWaves][kOut / 16];
     const int kvh = blockIdx.x, seq = blockIdx.y;
+    for (int e = threadIdx.x; e < kLutEntries; e += kThreads) lut[e] = A.lut[e];
+    for (int e = threadIdx.x; e < 256; e += kThreads) rlev[e] = A.rlev[kvh * 256 + e];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int t = lane >> 2, j = lane & 3;
     const int len = max(0, min(A.seq_lens[seq], A.max_pages * kPage));
     const int npages = (len + kPage - 1) / kPage;
     const int p_end = min(npages, (int)(blockIdx.z + 1) * kDecompChunk);
+    const int p0 = blockIdx.z * kDecompChunk + wave;       // this wave: pages p0 + kWaves * i
+    const int cnt = p_end > p0 ? (p_end - p0 + kWaves - 1) / kWaves : 0;
+    // page ids are int32: a 32-bit unsigned test against the pool size
+    // (capped at 2^31) is the range check, and stays on the scalar unit
+    const uint32_t npg32 = (uint32_t)min<int64_t>(A.num_pages, 0x80000000LL);
+    int btv = -1, hbv = 0;
+    uint64_t offv = 0;
+    if (lane < cnt) {
+        btv = A.block_table[(int64_t)seq * A.max_pages + p0 + kWaves * lane];
+        if (TB == 0 && (uint32_t)btv < npg32) {
+            hbv = A.page_bits[btv];
+            offv = A.page_off ? A.page_off[btv] : (uint64_t)btv * (uint64_t)A.page_stride;
+        }
+    }
+    uint32_t err = 0;
+    __syncthreads();
     struct Pg {
-        int ph, b;
         uint32_t cw[8];
-        uint32_t rc;
+        uint32_t rc, hb;
+        int ph, b, live;
     };
-    // header, codes and radius byte of page p (ph < 0: nothing to do)
-    auto fetch = [&](int p, Pg &g) {
-        g.ph = -1;
-        g.b = 0;
-        if (p >= p_end) return;
-        const int ph = A.block_table[(int64_t)seq * A.max_pages + p];
-        if (ph < 0 || (int64_t)ph >= A.num_pages) {
-            if (lane == 0) atomicOr(A.err, 2u);
-            return;
+    auto fetch = [&](int i, Pg &g) {
+        const int li = min(i, kPer - 1);
+        const int ph = __builtin_amdgcn_readlane(btv, li);
+        const bool inr = i < cnt;
+        const bool ok = inr && (uint32_t)ph < npg32;
+        err |= (inr && !ok) ? 2u : 0u;
+        const int phc = ok ? ph : 0;
+        int b = TB, KB = record_bytes(D, TB == 0 ? 8 : TB);
+        uint64_t off = (uint64_t)phc * (uint64_t)A.page_stride;
+        bool live = ok;
+        if (TB == 0) {
+            b = __builtin_amdgcn_readlane(hbv, li);
+            const bool tier_ok = b >= 2 && b <= 8 && ((A.tier_mask >> b) & 1u) && ((kSupportedTiers >> b) & 1u);
+            err |= (ok && !tier_ok) ? 4u : 0u;
+            live = ok && tier_ok;
+            KB = live ? record_bytes(D, b) : 0;
+            off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(offv >> 32), li) << 32) |
+                  __builtin_amdgcn_readlane((uint32_t)offv, li);
         }
-        const int b = A.page_bits[ph];
-        if (b < 2 || b > 8 || !((A.tier_mask >> b) & 1u) || !((kSupportedTiers >> b) & 1u)) {
-            if (lane == 0) atomicOr(A.err, 4u);
-            return;
-        }
-        const uint64_t off = A.page_off ? A.page_off[ph] : (uint64_t)ph * (uint64_t)A.page_stride;
-        const int KB = record_bytes(D, b);
-        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + off + (uint64_t)kvh * kPage * KB, kPage * KB);
+        // (the bases are read back as scalars: without that the compiler
+        // may form a 64-bit sum on the vector unit and then loop over lanes
+        // to build the descriptor)
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(scalar_ptr(A.kcode + off + (uint64_t)kvh * kPage * KB),
+                                                   __builtin_amdgcn_readfirstlane(live ? kPage * KB : 0));
+        const __amdgpu_buffer_rsrc_t rr = buf_rsrc(scalar_ptr(A.rcode + ((int64_t)phc * A.hkv + kvh) * kPage),
+                                                   __builtin_amdgcn_readfirstlane(live ? kPage : 0));
         const int vo = t * KB + j * (KB / 4);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 16 * k, 0, 0);
             g.cw[4 * k + 0] = x[0]; g.cw[4 * k + 1] = x[1]; g.cw[4 * k + 2] = x[2]; g.cw[4 * k + 3] = x[3];
         }
-        g.rc = A.rcode[((int64_t)ph * A.hkv + kvh) * kPage + t];
-        g.ph = ph;
+        g.rc = __builtin_amdgcn_raw_buffer_load_b8(rr, t, 0, 0);
+        if (TB != 0) {
+            // one tier: the header travels with the page and is checked
+            // before the stores
+            const __amdgpu_buffer_rsrc_t rh =
+                buf_rsrc(scalar_ptr(A.page_bits + phc), __builtin_amdgcn_readfirstlane(ok ? 1 : 0));
+            g.hb = __builtin_amdgcn_raw_buffer_load_b8(rh, 0, 0, 0);
+        } else {
+            g.hb = b;
+        }
+        g.ph = phc;
         g.b = b;
+        g.live = live ? 1 : 0;
     };
-    Pg cur, nxt;
-    int p = blockIdx.z * kDecompChunk + wave;
-    fetch(p, cur);
-    for (; p < p_end; p += kWaves) {
-        fetch(p + kWaves, nxt);
-        if (cur.ph >= 0) {
-            const float rr = A.rlev[kvh * 256 + cur.rc];
-            uint16_t *dst = A.kdense + (((int64_t)cur.ph * A.hkv + kvh) * kPage + t) * D + j * (D / 4);
-            switch (cur.b) {
-                case 2: decompress_slice<D, 2>(cur.cw, lut, rr, dst); break;
-                case 3: decompress_slice<D, 3>(cur.cw, lut, rr, dst); break;
-                case 4: decompress_slice<D, 4>(cur.cw, lut, rr, dst); break;
-                case 6: decompress_slice<D, 6>(cur.cw, lut, rr, dst); break;
-                default: decompress_slice<D, 8>(cur.cw, lut, rr, dst); break;
+    auto emit = [&](const Pg &g) {
+        bool st = g.live;
+        if (TB != 0) {
+            const bool hdr_ok = __builtin_amdgcn_readfirstlane(g.hb) == TB;
+            err |= (g.live && !hdr_ok) ? 4u : 0u;
+            st = g.live && hdr_ok;
+        }
+        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(scalar_ptr(A.kdense + ((int64_t)g.ph * A.hkv + kvh) * (kPage * D)),
+                                                   __builtin_amdgcn_readfirstlane(st ? kOut : 0));
+        uint32_t pk[D / 8];
+        const float rr = rlev[g.rc & 255u];
+        if (TB != 0) {
+            decompress_pack<D, TB>(g.cw, lut, rr, pk);
+        } else {
+            switch (g.b) {
+                case 2: decompress_pack<D, 2>(g.cw, lut, rr, pk); break;
+                case 3: decompress_pack<D, 3>(g.cw, lut, rr, pk); break;
+                case 4: decompress_pack<D, 4>(g.cw, lut, rr, pk); break;
+                case 6: decompress_pack<D, 6>(g.cw, lut, rr, pk); break;
+                default: decompress_pack<D, 8>(g.cw, lut, rr, pk); break;
             }
         }
-        cur = nxt;
+        // The lane's D/4 values are 16-byte pieces at a 64-byte lane stride
+        // (token t, quarter j); stored straight from the lanes every store
+        // would scatter 16-byte pieces.  The 16-byte slots of the stage are
+        // swizzled (bits 0-1 of the slot index XOR bits 4-5), which spreads
+        // both the lane-strided writes and the contiguous reads over
+        // distinct LDS banks.
+        uint4 *sw = stage[wave];
+        auto slot = [](int idx) { return idx ^ ((idx >> 4) & 3); };
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k)
+            sw[slot(t * (D / 8) + j * (D / 32) + k)] = make_uint4(pk[4 * k], pk[4 * k + 1], pk[4 * k + 2], pk[4 * k + 3]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+            const uint4 x = sw[slot(k * 64 + lane)];
+            const __attribute__((ext_vector_type(4))) uint32_t v4 = {x.x, x.y, x.z, x.w};
+            __builtin_amdgcn_raw_buffer_store_b128(v4, rd, (k * 64 + lane) * 16, 0, kStoreNT);
+        }
+        // (the next page's writes to the stage come after these reads)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // (the scheduling barriers keep each page's loads issued ahead of the
+    // wait for the page before)
+    Pg b0, b1;
+    fetch(0, b0);
+    {
+        // stores through an empty descriptor (dropped): on entry the queue of
+        // memory operations then looks as it does on every later turn of the
+        // loop (a page's loads, then D/32 stores), so the wait counts
+        // computed for the loop need not cover the stores
+        const __amdgpu_buffer_rsrc_t rz = buf_rsrc(A.kdense, 0);
+        const __attribute__((ext_vector_type(4))) uint32_t z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) __builtin_amdgcn_raw_buffer_store_b128(z4, rz, 16 * k, 0, kStoreNT);
     }
+    // two buffers used in turn (no register copies, which would wait for
+    // the loads in flight and the stores before them)
+#pragma unroll 1
+    for (int i = 0; i < cnt; i += 2) {
+        fetch(i + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        emit(b0);
+        fetch(i + 2, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        emit(b1);
+    }
+    if (err && lane == 0) atomicOr(A.err, err);
 }
 
 hipError_t launch_decompress(const DecodeArgs &a, int d, int B, hipStream_t s) {
     if (B == 0) return hipSuccess;
     const dim3 grid((unsigned)a.hkv, (unsigned)B, (unsigned)((a.max_pages + kDecompChunk - 1) / kDecompChunk));
-    if (d == 128) hipLaunchKernelGGL(k_decompress<128>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_decompress<64>, grid, dim3(kThreads), 0, s, a);
+    int tb = 0;
+    if (__builtin_popcount(a.tier_mask) == 1 && !a.page_off) tb = __builtin_ctz(a.tier_mask);
+#define SKA_DECOMP(DD)                                                                              \
+    switch (tb) {                                                                                   \
+        case 2: hipLaunchKernelGGL((k_decompress<DD, 2>), grid, dim3(kThreads), 0, s, a); break;    \
+        case 3: hipLaunchKernelGGL((k_decompress<DD, 3>), grid, dim3(kThreads), 0, s, a); break;    \
+        case 4: hipLaunchKernelGGL((k_decompress<DD, 4>), grid, dim3(kThreads), 0, s, a); break;    \
+        case 6: hipLaunchKernelGGL((k_decompress<DD, 6>), grid, dim3(kThreads), 0, s, a); break;    \
+        case 8: hipLaunchKernelGGL((k_decompress<DD, 8>), grid, dim3(kThreads), 0, s, a); break;    \
+        default: hipLaunchKernelGGL((k_decompress<DD, 0>), grid, dim3(kThreads), 0, s, a); break;   \
+    }
+    if (d == 128) {
+        SKA_DECOMP(128)
+    } else {
+        SKA_DECOMP(64)
+    }
+#undef SKA_DECOMP
     return hipGetLastError();
 }
 
