@@ -176,6 +176,8 @@ def main():
                     help="also time ADA and dense bf16 at T = 8K, 32K, 128K with gqa_t32k's batch shape")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the dense-bf16 and decompress-then-dot timings on the same pages")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip the timing of the decode step with append (ska_append_decode_attention)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle timing")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain copy kernel of this many MiB (counter calibration)")
@@ -320,6 +322,31 @@ def main():
                             "vs_decompress_then_dot": round(ms_dtd / ms_per_step, 3)},
         }
 
+    append = None
+    if not args.no_append:
+        # the decode step with append: each sequence's token at position
+        # seq_len - 1 is encoded into its slot (a synthetic new token over the
+        # last one resident), then the same decode
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        nk = torch.randn((w.B, w.hkv, w.d), device=dev, generator=g)
+        nv = torch.randn((w.B, w.hkv, w.d), device=dev, generator=g).to(torch.bfloat16).view(torch.int16)
+
+        def run_append(i):
+            ska.append_decode_attention(caches[i % nc], nk, nv, q, bt, sl, num_splits=args.splits, out=out)
+
+        for i in range(args.warmup):
+            run_append(i)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            run_append(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_app = ev0.elapsed_time(ev1) / args.steps
+        log("decode step with append: %.2f us/step" % (ms_app * 1e3))
+        append = {"us_per_step": round(ms_app * 1e3, 2), "extra_us_vs_decode": round((ms_app - ms_per_step) * 1e3, 2)}
+
     sweep = None
     if args.sweep_context:
         del caches, kdense
@@ -357,6 +384,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "baselines": baselines,
+        "append_step": append,
         "context_sweep": sweep,
     }
     print(json.dumps(line), flush=True)

@@ -137,6 +137,34 @@ ska_status ska_decode_attention(ska_cache *cache, const float *q, int batch, int
                                 const int32_t *seq_lens, float scale, int num_splits,
                                 float *out, float *logits_dbg, void *stream);
 
+/* ska_append_decode_attention -- a decode step that first stores the step's
+ * new token (the write path of section 2.3, dense key -> spherical codes ->
+ * paged store, run inside the step), then decodes over all tokens including
+ * it, exactly as ska_decode_attention.
+ *   new_keys    device fp32 [batch][Hkv][d]: the new token's key of each
+ *               sequence
+ *   new_values  device bf16 [batch][Hkv][d]: its values
+ *   seq_lens    device int32 [batch]: lengths including the new token; the
+ *               new token of sequence s goes to position seq_lens[s] - 1
+ *               (page block_table[s][(seq_lens[s]-1)/16], slot
+ *               (seq_lens[s]-1)%16), encoded at that page's tier
+ *               (page_bits, and page_off for variable-size pages, must be
+ *               set for a new page first).  seq_lens[s] <= 0 appends nothing.
+ *   other arguments as ska_decode_attention.
+ * One kernel on `stream`: inside the decode, the wave that reads the new
+ * token's page for a KV head first stores the token there (codes, radius
+ * code, values, as ska_encode_keys would at the cache's radius range).  A
+ * position past the row or a block-table entry outside the pool sets
+ * SKA_DEVERR_SLOT (nothing is stored for that sequence); a page header
+ * outside tier_mask sets SKA_DEVERR_TIER.  Argument errors are those of
+ * ska_decode_attention, plus SKA_ERR_INVALID for NULL new_keys/new_values
+ * with batch > 0; a rejected call stores nothing.  Returns SKA_OK. */
+ska_status ska_append_decode_attention(ska_cache *cache, const float *new_keys, const uint16_t *new_values,
+                                       const float *q, int batch, int num_q_heads,
+                                       const int32_t *block_table, int max_pages,
+                                       const int32_t *seq_lens, float scale, int num_splits,
+                                       float *out, float *logits_dbg, void *stream);
+
 /* ska_dense_decode_attention -- the baseline the codes replace (section 1 of
  * the page: decode streams dense KV pages from HBM): the same decode step as
  * ska_decode_attention over keys stored densely as bf16, with the cache's

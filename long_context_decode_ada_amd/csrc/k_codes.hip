@@ -51,14 +51,12 @@ hipError_t launch_calibrate(const float *keys, int64_t n, int hkv, int d, unsign
 // row, then the record is packed slice by slice into 32-bit words.
 constexpr int kEncThreads = 128;
 
-__global__ __launch_bounds__(kEncThreads) void k_encode(EncodeArgs A) {
-    __shared__ uint8_t codes_lds[kEncThreads][128];
-    const int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
-    if (i >= A.n * A.hkv) return;
+// Encodes key x (d fp32) of KV head g into pool slot `slot` (phys*16 + s) at
+// the tier of its page, with its values vs (d bf16) when given.  cl: a
+// 128-byte scratch row.
+__device__ void encode_one(const EncodeArgs &A, const float *__restrict__ x, const uint16_t *__restrict__ vs,
+                           int g, int64_t slot, uint8_t *cl) {
     const int d = A.d;
-    const int64_t tok = i / A.hkv;
-    const int g = (int)(i % A.hkv);
-    const int64_t slot = A.slot[tok];
     const int64_t phys = slot >> 4;
     const int s = (int)(slot & 15);
     if (slot < 0 || phys >= A.num_pages) {
@@ -70,8 +68,6 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(EncodeArgs A) {
         atomicOr(A.err, 4u);
         return;
     }
-    uint8_t *cl = codes_lds[threadIdx.x];
-    const float *x = A.keys + i * d;
     const double *c2 = A.tab.cos2 + thr_off(b), *s2 = A.tab.sin2 + thr_off(b);
     const double *c2h = A.tab.cos2 + thr_off(b - 1), *s2h = A.tab.sin2 + thr_off(b - 1);
 
@@ -116,11 +112,19 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(EncodeArgs A) {
         }
     }
     A.rcode[((uint64_t)phys * A.hkv + g) * kPage + s] = (uint8_t)rc;
-    if (A.values) {
-        const uint16_t *vs = A.values + i * d;
+    if (vs) {
         uint16_t *vd = A.v + ((uint64_t)phys * A.hkv + g) * (uint64_t)d * kPage + s;
         for (int e = 0; e < d; ++e) vd[(uint64_t)e * kPage] = vs[e];
     }
+}
+
+__global__ __launch_bounds__(kEncThreads) void k_encode(EncodeArgs A) {
+    __shared__ uint8_t codes_lds[kEncThreads][128];
+    const int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
+    if (i >= A.n * A.hkv) return;
+    const int64_t tok = i / A.hkv;
+    const int g = (int)(i % A.hkv);
+    encode_one(A, A.keys + i * A.d, A.values ? A.values + i * A.d : nullptr, g, A.slot[tok], codes_lds[threadIdx.x]);
 }
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {

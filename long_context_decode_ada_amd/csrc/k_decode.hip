@@ -610,9 +610,108 @@ __device__ __forceinline__ void load_query(const uint4 *src, uint32_t (&u)[D * G
     }
 }
 
+// The decode step with append: the wave whose page run holds position
+// len - 1 (the new token) first stores the token there for its KV head --
+// angle codes at the page's tier, record, radius code, values, exactly as
+// the encoder writes them (the write path of section 2.3 of the page) -- and
+// only then reads that page, so the decode sees it like any stored token.
+// The suffix sums of squares run in one lane from the last component
+// backwards (the defining order); the lanes then decide the codes against
+// the edge tables already in LDS, pack the record's 32-bit words and store
+// the values.  Nothing else in the call reads this (page, KV head), so a
+// workgroup-scope fence orders the stores before the wave's own page loads.
+// S: D doubles of LDS scratch, cl: D bytes of LDS scratch (this wave's).
+template <int D, int TB>
+__device__ __forceinline__ void append_token(const DecodeArgs &A, int seq, int kvh, int len_in, int ph,
+                                             const float *xk, const double *tau2, const double *c2s,
+                                             const double *s2s, double *S, uint8_t *cl) {
+    const int lane = threadIdx.x & 63;
+    constexpr int PL = D / 64;
+    if (len_in > A.max_pages * kPage) {   // past the block-table row: nothing stored
+        if (lane == 0) atomicOr(A.err, 1u);
+        return;
+    }
+    if (ph < 0 || (int64_t)ph >= A.num_pages) {
+        if (lane == 0) atomicOr(A.err, 1u);
+        return;
+    }
+    const int pos = len_in - 1, s = pos % kPage;
+    // (the header is read now and checked before the stores; with a single
+    // tier the codes need not wait for it)
+    const int hb = A.page_bits[ph];
+    const int b = TB != 0 ? TB : hb;
+    if (TB == 0 && !(b >= 2 && b <= 8 && ((A.tier_mask >> b) & 1u))) {
+        if (lane == 0) atomicOr(A.err, 4u);
+        return;
+    }
+    const uint64_t off = (TB == 0 && A.page_off) ? A.page_off[ph] : (uint64_t)ph * (uint64_t)A.page_stride;
+    if (lane == 0) {
+        double T = add_square(0.0, xk[D - 1]);
+        T = add_square(T, xk[D - 2]);
+#pragma unroll
+        for (int a = D - 3; a >= 0; --a) {
+            S[a] = T;
+            T = add_square(T, xk[a]);
+        }
+        S[D - 1] = T;   // |k|^2 (S[D-1] itself is not a suffix sum any code uses)
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+    for (int r = 0; r < PL; ++r) {
+        const int a = lane * PL + r;
+        if (a < D - 2) cl[a] = (uint8_t)polar_code((double)xk[a], S[a], b, c2s + thr_off(b), s2s + thr_off(b));
+        else if (a == D - 2)
+            cl[a] = (uint8_t)azimuth_code((double)xk[D - 2], (double)xk[D - 1], b, c2s + thr_off(b - 1),
+                                          s2s + thr_off(b - 1));
+    }
+    const double Tall = S[D - 1];
+    // radius code = #{j : |k|^2 >= tau2[j]} (tau2 increases with j)
+    int rc = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int j = lane + 64 * k;
+        rc += __popcll(__builtin_amdgcn_ballot_w64(j < 255 && Tall >= tau2[min(j, 254)]));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (TB != 0 && hb != TB) {
+        if (lane == 0) atomicOr(A.err, 4u);
+        return;
+    }
+    // the record: slice sl holds the codes of angles [sl*na, min((sl+1)*na,
+    // D-1)) as one bit string, b bits each, least significant first; word wi
+    // of a slice is bits [32 wi, 32 wi + 32) of that string
+    const int kb = record_bytes(D, b), wps = kb / 16;
+    constexpr int na = D / 4;
+    uint32_t *rec = reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(A.kcode) + off +
+                                                 ((uint64_t)kvh * kPage + s) * kb);
+    for (int wq = lane; wq < 4 * wps; wq += 64) {
+        const int sl = wq / wps, bit0 = 32 * (wq % wps);
+        const int a0 = sl * na, a1 = min((sl + 1) * na, D - 1);
+        uint32_t word = 0;
+        for (int k = bit0 / b; a0 + k < a1 && k * b < bit0 + 32; ++k) {
+            const int sh = k * b - bit0;
+            const uint32_t c = cl[a0 + k];
+            word |= sh >= 0 ? (c << sh) : (c >> -sh);
+        }
+        rec[wq] = word;
+    }
+    if (lane == 0) const_cast<uint8_t *>(A.rcode)[((int64_t)ph * A.hkv + kvh) * kPage + s] = (uint8_t)rc;
+    const uint16_t *vs = A.app_v + ((int64_t)seq * A.hkv + kvh) * D;
+    uint16_t *vd = const_cast<uint16_t *>(A.v) + ((int64_t)ph * A.hkv + kvh) * (int64_t)D * kPage + s;
+    for (int e = lane; e < D; e += 64) vd[(int64_t)e * kPage] = vs[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // TB: the angle bit width of every page when the pool has a single tier, or 0
-// (pages of mixed tiers, dispatched per page on the header).
-template <int D, int G, int TB, bool DBG>
+// (pages of mixed tiers, dispatched per page on the header).  APP: the decode
+// step with append (append_token).
+template <int D, int G, int TB, bool DBG, bool APP = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_decode(DecodeArgs A) {
     constexpr int NA = D / 4;
     constexpr int NT = D / 16;
@@ -641,6 +740,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __shared__ double c2s[kThrEntries], s2s[kThrEntries];
     __shared__ __attribute__((aligned(16))) _Float16 uq_lds[(TB == 0 ? 5 : 1) * D * G];
     __shared__ float sq_lds[G];
+    // append: the new token's key for this KV head and the head's radius edges
+    __shared__ float akey[APP ? D : 1];
+    __shared__ double atau2[APP ? 256 : 1];
 
     // ---- prologue.  Every global read it needs is issued at once: the
     // sequence length, the block-table entries of this wave's run (taken as
@@ -687,9 +789,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
     for (int i = 0; i < kNQ; ++i) st_q[i] = A.q[head0 * D + min(tid + i * kThreads, G * D - 1)];
     const float st_r = A.rlev[kvh * 256 + (tid & 255)];
+    float st_k = 0.f;
+    double st_t = 0.0;
+    if constexpr (APP) {
+        st_k = A.app_k[((int64_t)seq * A.hkv + kvh) * D + min(tid, D - 1)];
+        st_t = A.tau2[255 * kvh + min(tid, 254)];
+    }
     int len = A.seq_lens[seq];
     __builtin_amdgcn_sched_barrier(0);   // (every load above is issued before the wait for len)
 
+    const int len_in = len;   // (append: a length past the row is an error, not clamped)
     len = max(0, min(len, A.max_pages * kPage));
     const int npages = (len + kPage - 1) / kPage;
     if (p0 >= npages) {   // whole workgroup, before any barrier
@@ -708,6 +817,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
         for (int i = 0; i < kNQ; ++i) keep(st_q[i]);
         keep(st_r);
+        if constexpr (APP) {
+            keep(st_k);
+            keep(st_t);
+        }
         // a sequence with no resident token: its output rows are 0
         if (npages == 0 && split == 0)
             for (int e = threadIdx.x; e < G * D; e += kThreads) A.out[head0 * D + e] = 0.f;
@@ -739,6 +852,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         qs[e / D][e % D] = st_q[i];
     }
     rlev[tid & 255] = st_r;
+    if constexpr (APP) {
+        akey[min(tid, D - 1)] = st_k;
+        atau2[min(tid, 255)] = st_t;
+    }
 
     // The wave's page list, 64 pages at a time, one page per lane: valid
     // pages first (ordered by tier when tiers are mixed, so that the query
@@ -861,6 +978,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+
+    if constexpr (APP) {
+        // the wave whose run holds the new token's page stores the token
+        // first; with a single tier its first kBufs pages were requested
+        // above, so if the new page is among them they are requested again
+        const int pnew = (len - 1) / kPage;
+        if (pnew >= wp0 && pnew < wp1) {
+            // the page's id: among this wave's staged block-table entries
+            // (one per lane from p0 + wofs) when it is within the first 64
+            const int rel = pnew - (p0 + wofs);
+            const int ph_new = rel < 64 ? __builtin_amdgcn_readlane(ph_raw, rel) : A.block_table[bt_row + pnew];
+            append_token<D, TB>(A, seq, kvh, len_in, ph_new, akey, atau2, c2s, s2s, qT[wave],
+                                reinterpret_cast<uint8_t *>(mo[wave][0]));
+            if constexpr (TB != 0) {
+                if (pnew - wp0 < kBufs) {
+#pragma unroll
+                    for (int i = 0; i < kBufs; ++i) load_page<D, TB>(A, dd[i], kvh, R[i]);
+                }
+            }
+        }
+    }
 
     // Query prep, section 2.1's c_q: per tier, the angle codes of each query
     // row and the decoded direction u_a = (prod_{k<a} sin c_k) * cos c_a
@@ -1461,6 +1599,21 @@ hipError_t launch_decompress(const DecodeArgs &a, int d, int B, hipStream_t s) {
 
 template <int D, int G>
 static void launch_dg(const DecodeArgs &a, int tb, dim3 grid, hipStream_t s) {
+    if (a.app_k) {   // the decode step with append (never the dense keys)
+        if (a.logits) {
+            hipLaunchKernelGGL((k_decode<D, G, 0, true, true>), grid, dim3(kThreads), 0, s, a);
+            return;
+        }
+        switch (tb) {
+            case 2: hipLaunchKernelGGL((k_decode<D, G, 2, false, true>), grid, dim3(kThreads), 0, s, a); break;
+            case 3: hipLaunchKernelGGL((k_decode<D, G, 3, false, true>), grid, dim3(kThreads), 0, s, a); break;
+            case 4: hipLaunchKernelGGL((k_decode<D, G, 4, false, true>), grid, dim3(kThreads), 0, s, a); break;
+            case 6: hipLaunchKernelGGL((k_decode<D, G, 6, false, true>), grid, dim3(kThreads), 0, s, a); break;
+            case 8: hipLaunchKernelGGL((k_decode<D, G, 8, false, true>), grid, dim3(kThreads), 0, s, a); break;
+            default: hipLaunchKernelGGL((k_decode<D, G, 0, false, true>), grid, dim3(kThreads), 0, s, a); break;
+        }
+        return;
+    }
     if (a.logits) {  // debug variant: stores the logits; generic tier dispatch
         if (tb == kDenseTB) hipLaunchKernelGGL((k_decode<D, G, kDenseTB, true>), grid, dim3(kThreads), 0, s, a);
         else hipLaunchKernelGGL((k_decode<D, G, 0, true>), grid, dim3(kThreads), 0, s, a);

@@ -295,6 +295,29 @@ const char *ska_status_string(ska_status s) {
     return "unknown status";
 }
 
+namespace {
+
+// the pool side of the encode arguments (keys, values and slots left empty)
+EncodeArgs encode_args(const ska_cache *c) {
+    EncodeArgs a{};
+    a.d = c->pool.d;
+    a.hkv = c->pool.num_kv_heads;
+    a.num_pages = c->pool.num_pages;
+    a.tier_mask = c->pool.tier_mask;
+    a.page_bits = c->pool.page_bits;
+    a.page_off = c->pool.page_off;
+    a.page_stride = c->page_stride;
+    a.kcode = c->pool.kcode;
+    a.rcode = c->pool.rcode;
+    a.v = c->pool.v;
+    a.tau2 = c->d_tau2;
+    a.tab = CodeTables{c->d_cos2, c->d_sin2, c->d_cen};
+    a.err = c->d_err;
+    return a;
+}
+
+}  // namespace
+
 ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool, const float *keys,
                            const uint16_t *values, const int64_t *slot, int64_t n,
                            const double *radius_range, void *stream) {
@@ -325,24 +348,11 @@ ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool, const f
     }
     c->pool = *pool;  // same shape; pointers may move
     if (n > 0) {
-        EncodeArgs a{};
+        EncodeArgs a = encode_args(c);
         a.keys = keys;
         a.values = values;
         a.slot = slot;
         a.n = n;
-        a.d = pool->d;
-        a.hkv = pool->num_kv_heads;
-        a.num_pages = pool->num_pages;
-        a.tier_mask = pool->tier_mask;
-        a.page_bits = pool->page_bits;
-        a.page_off = pool->page_off;
-        a.page_stride = c->page_stride;
-        a.kcode = pool->kcode;
-        a.rcode = pool->rcode;
-        a.v = pool->v;
-        a.tau2 = c->d_tau2;
-        a.tab = CodeTables{c->d_cos2, c->d_sin2, c->d_cen};
-        a.err = c->d_err;
         if (launch_encode(a, s) != hipSuccess) {
             if (created) release(c);
             return SKA_ERR_HIP;
@@ -358,7 +368,8 @@ namespace {
 // the dense baseline, over bf16 keys k_dense with the cache's values.
 ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, int batch, int num_q_heads,
                        const int32_t *block_table, int max_pages, const int32_t *seq_lens,
-                       float scale, int num_splits, float *out, float *logits_dbg, void *stream) {
+                       float scale, int num_splits, float *out, float *logits_dbg, void *stream,
+                       const float *app_k = nullptr, const uint16_t *app_v = nullptr) {
     if (!c) return SKA_ERR_INVALID;
     if (batch < 0 || num_q_heads < 1 || max_pages < 1 || num_splits < 0) return SKA_ERR_INVALID;
     if (!std::isfinite(scale) || scale < 0.f) return SKA_ERR_INVALID;
@@ -441,6 +452,9 @@ ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, in
     da.tier_mask = c->pool.tier_mask;
     da.nt = c->nt;
     for (int b = 0; b <= 8; ++b) da.tslot[b] = c->tslot[b];
+    da.app_k = app_k;
+    da.app_v = app_v;
+    da.tau2 = c->d_tau2;
     if (launch_decode(da, d, G, batch, s) != hipSuccess) return SKA_ERR_HIP;
     if (ev && hipEventRecord(ev[1], s) != hipSuccess) return SKA_ERR_HIP;
 
@@ -454,6 +468,24 @@ ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num
                                 float scale, int num_splits, float *out, float *logits_dbg, void *stream) {
     return decode_impl(c, nullptr, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale, num_splits,
                        out, logits_dbg, stream);
+}
+
+ska_status ska_append_decode_attention(ska_cache *c, const float *new_keys, const uint16_t *new_values,
+                                       const float *q, int batch, int num_q_heads, const int32_t *block_table,
+                                       int max_pages, const int32_t *seq_lens, float scale, int num_splits,
+                                       float *out, float *logits_dbg, void *stream) {
+    if (!c) return SKA_ERR_INVALID;
+    if (batch > 0 && (!new_keys || !new_values || !block_table || !seq_lens)) return SKA_ERR_INVALID;
+    if (batch < 0 || max_pages < 1) return SKA_ERR_INVALID;
+    // the decode's own checks first, so that a rejected call writes nothing
+    if (num_q_heads < 1 || num_q_heads % c->pool.num_kv_heads != 0 || num_splits < 0) return SKA_ERR_INVALID;
+    const int G = num_q_heads / c->pool.num_kv_heads;
+    if (G != 1 && G != 2 && G != 4) return SKA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale) || scale < 0.f) return SKA_ERR_INVALID;
+    if (batch > 0 && (!q || !out)) return SKA_ERR_INVALID;
+    if (batch > 65535 || (int64_t)batch * num_q_heads > (1ll << 30)) return SKA_ERR_UNSUPPORTED;
+    return decode_impl(c, nullptr, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale, num_splits,
+                       out, logits_dbg, stream, new_keys, new_values);
 }
 
 ska_status ska_dense_decode_attention(ska_cache *c, const uint16_t *k_dense, const float *q, int batch,

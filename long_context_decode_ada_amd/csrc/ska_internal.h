@@ -109,6 +109,11 @@ struct DecodeArgs {
     int8_t tslot[9];         // tier b -> index among the tiers present
     float scale;             // softmax scale
     int query_mode;          // 0: coded query, 1: exact query direction
+    // decode step with append (else NULL): the new token of each sequence,
+    // stored at position seq_lens[s] - 1 before that page is read
+    const float *app_k;      // [B][hkv][d]
+    const uint16_t *app_v;   // [B][hkv][d] bf16
+    const double *tau2;      // [hkv][255] squared radius edges
 };
 
 

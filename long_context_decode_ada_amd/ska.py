@@ -22,9 +22,9 @@ Q_CODED, Q_EXACT = 0, 1
 PAGE = 16
 DEVERR_SLOT, DEVERR_PAGE, DEVERR_TIER = 1, 2, 4
 
-SYMBOLS = ("ska_encode_keys", "ska_decode_attention", "ska_dense_decode_attention", "ska_decompress_keys",
-           "ska_rdr_plan", "ska_get_radius_range", "ska_device_errors", "ska_profile_begin", "ska_profile_read",
-           "ska_free", "ska_status_string")
+SYMBOLS = ("ska_encode_keys", "ska_decode_attention", "ska_append_decode_attention", "ska_dense_decode_attention",
+           "ska_decompress_keys", "ska_rdr_plan", "ska_get_radius_range", "ska_device_errors",
+           "ska_profile_begin", "ska_profile_read", "ska_free", "ska_status_string")
 
 
 class SkaError(RuntimeError):
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.ska_encode_keys.argtypes = [ctypes.POINTER(P), ctypes.POINTER(PoolDesc), P, P, P, i64, P, P]
         L.ska_decode_attention.restype = i
         L.ska_decode_attention.argtypes = [P, P, i, i, P, i, P, f, i, P, P, P]
+        L.ska_append_decode_attention.restype = i
+        L.ska_append_decode_attention.argtypes = [P, P, P, P, i, i, P, i, P, f, i, P, P, P]
         L.ska_dense_decode_attention.restype = i
         L.ska_dense_decode_attention.argtypes = [P, P, P, i, i, P, i, P, f, i, P, P, P]
         L.ska_decompress_keys.restype = i
@@ -187,6 +189,23 @@ def decode_attention(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, s
                                    _ptr(seq_lens), float(scale), int(num_splits), _ptr(out), _ptr(logits),
                                    _stream(stream))
     _check(s, "ska_decode_attention")
+    return out
+
+
+def append_decode_attention(cache: Cache, new_keys: torch.Tensor, new_values: torch.Tensor, q: torch.Tensor,
+                            block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float = 0.0,
+                            num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                            logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ska_append_decode_attention: new_keys fp32 [B][hkv][d] and new_values bf16 bits [B][hkv][d] (int16
+    view) are stored at position seq_lens[s]-1 of each sequence (seq_lens include them), then the decode
+    as decode_attention."""
+    B, hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    s = lib().ska_append_decode_attention(cache.handle, _ptr(new_keys), _ptr(new_values), _ptr(q), B, hq,
+                                          _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
+                                          float(scale), int(num_splits), _ptr(out), _ptr(logits), _stream(stream))
+    _check(s, "ska_append_decode_attention")
     return out
 
 

@@ -85,6 +85,12 @@ def test_decode_rejects_bad_arguments_without_a_cache():
     assert L.ska_decode_attention(None, 16, 1, 32, 16, 4, 16, 0.0, 0, 16, None, None) == ska.SKA_ERR_INVALID
 
 
+def test_append_rejects_bad_arguments_without_a_cache():
+    L = ska.lib()
+    assert L.ska_append_decode_attention(None, 16, 16, 16, 1, 32, 16, 4, 16, 0.0, 0, 16, None,
+                                         None) == ska.SKA_ERR_INVALID
+
+
 def test_null_free_and_queries():
     L = ska.lib()
     L.ska_free(None)
