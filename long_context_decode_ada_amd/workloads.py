@@ -67,8 +67,8 @@ class Workload:
     seq_lens: np.ndarray            # int32 [B] resident tokens
     block_table: np.ndarray         # int32 [B][max_pages]
     num_pages: int
-    page_bits: np.ndarray           # uint8 [num_pages]
-    page_off: Optional[np.ndarray]  # uint64 [num_pages] or None
+    page_bits: np.ndarray           # uint8 [num_pages] ([num_pages*hkv] with head_tiers)
+    page_off: Optional[np.ndarray]  # uint64 [num_pages] ([num_pages*hkv] with head_tiers) or None
     bstride: int                    # tier used for the fixed page stride when page_off is None
     kcode_bytes: int
     keys: np.ndarray                # float32 [n][hkv][d]
@@ -77,6 +77,7 @@ class Workload:
     q: np.ndarray                   # float32 [B][hq][d]
     scale: float = 0.0              # 0 => 1/sqrt(d)
     seed: int = SEED
+    head_tiers: bool = False        # tiers per (page, KV head): header and offset of each head's records
 
     @property
     def max_pages(self) -> int:
@@ -98,8 +99,9 @@ class Workload:
             for p in range(npg):
                 phys = int(self.block_table[s, p])
                 ntok = min(PAGE, n - p * PAGE)
-                b = int(self.page_bits[phys])
-                tot += self.hkv * ntok * (record_bytes(self.d, b) + 1 + 2 * self.d)
+                for g in range(self.hkv):
+                    b = int(self.page_bits[phys * self.hkv + g] if self.head_tiers else self.page_bits[phys])
+                    tot += ntok * (record_bytes(self.d, b) + 1 + 2 * self.d)
                 tot += self.hkv * (4 + 1 + (8 if self.page_off is not None else 0))
         tot += self.B * self.hq * self.d * 4 * 2
         return tot
@@ -157,18 +159,22 @@ def _streams(idx: int, n: int = 10):
 
 
 def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool = True,
-         tiers: Optional[tuple] = None) -> Workload:
+         tiers: Optional[tuple] = None, head_tiers: bool = False) -> Workload:
     """Build one workload.  ``scale`` < 1 shrinks the context (and, for
     ragged_b64, the lengths) for oracle-sized tests; ``batch`` overrides B;
     ``data=False`` builds the page structure only (empty keys/values/query);
     ``tiers`` (mixed_tiers only) replaces the tier set {2,4,6,8} by the given
-    widths, drawn with equal probability (the sink page takes the widest).
-    Every part draws from its own seeded stream, so the structure does not
-    depend on ``data``."""
+    widths, drawn with equal probability (the sink page takes the widest);
+    ``head_tiers`` (mixed_tiers only) draws the tier per (page, KV head)
+    instead of per page (the sink page's heads all take the widest), with a
+    header and a record offset per (page, KV head).  Every part draws from
+    its own seeded stream, so the structure does not depend on ``data``."""
     if name not in NAMES:
         raise KeyError(name)
     if tiers is not None and name != "mixed_tiers":
         raise ValueError("tiers applies to mixed_tiers only")
+    if head_tiers and name != "mixed_tiers":
+        raise ValueError("head_tiers applies to mixed_tiers only")
     tiers_override = tiers
     idx = NAMES.index(name)
     r_keys, r_vals, r_q, r_len, r_pages, r_tier, r_evict, r_scale, _, _ = _streams(idx)
@@ -204,10 +210,11 @@ def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool 
         if name == "mixed_tiers":
             T = int(lens[s])
             npg = (T + PAGE - 1) // PAGE
+            shape = (npg, hkv) if head_tiers else npg
             if tiers_override is None:
-                tier = r_tier.choice(np.array([2, 4, 6, 8]), size=npg, p=[0.3, 0.4, 0.2, 0.1])
+                tier = r_tier.choice(np.array([2, 4, 6, 8]), size=shape, p=[0.3, 0.4, 0.2, 0.1])
             else:
-                tier = r_tier.choice(np.array(sorted(tiers)), size=npg)
+                tier = r_tier.choice(np.array(sorted(tiers)), size=shape)
             tier[0] = max(tiers)                          # sink page: protected, b_max
             nonsink = np.arange(1, npg)
             evict = r_evict.choice(nonsink, size=len(nonsink) // 2, replace=False)
@@ -237,13 +244,22 @@ def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool 
         num_pages = total_pages
         perm = r_pages.permutation(num_pages)
     block_table = np.zeros((B, max_pages), np.int32)
-    page_bits = np.full(num_pages, max(tiers), np.uint8)
+    page_bits = np.full((num_pages, hkv) if head_tiers else num_pages, max(tiers), np.uint8)
     k = 0
     for s in range(B):
         block_table[s, : npages[s]] = perm[k: k + npages[s]]
         page_bits[perm[k: k + npages[s]]] = tier_list[s]
         k += npages[s]
-    if len(tiers) > 1:
+    if head_tiers:
+        # one header and one record offset per (page, KV head), packed in
+        # (page, head) order
+        page_bits = page_bits.reshape(-1)
+        sizes = PAGE * np.array([record_bytes(d, int(b)) for b in page_bits], np.uint64)
+        page_off = np.zeros(num_pages * hkv, np.uint64)
+        page_off[1:] = np.cumsum(sizes)[:-1]
+        kcode_bytes = int(sizes.sum())
+        bstride = max(tiers)
+    elif len(tiers) > 1:
         sizes = hkv * PAGE * np.array([record_bytes(d, int(b)) for b in page_bits], np.uint64)
         page_off = np.zeros(num_pages, np.uint64)
         page_off[1:] = np.cumsum(sizes)[:-1]
@@ -289,7 +305,7 @@ def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool 
                     tier_mask=sum(1 << b for b in tiers), seq_lens=lens,
                     block_table=block_table, num_pages=num_pages, page_bits=page_bits,
                     page_off=page_off, bstride=bstride, kcode_bytes=kcode_bytes,
-                    keys=keys, values=values, slot=slot, q=q)
+                    keys=keys, values=values, slot=slot, q=q, head_tiers=head_tiers)
 
 
 def host_pools(w: Workload, poison: bool = True) -> dict:
@@ -298,7 +314,7 @@ def host_pools(w: Workload, poison: bool = True) -> dict:
     fill8 = 0xFF if poison else 0
     return {
         "d": w.d, "hkv": w.hkv, "bstride": w.bstride,
-        "page_bits": w.page_bits, "page_off": w.page_off,
+        "page_bits": w.page_bits, "page_off": w.page_off, "head_tiers": w.head_tiers,
         "kcode": np.full(w.kcode_bytes, fill8, np.uint8),
         "rcode": np.full(w.num_pages * w.hkv * PAGE, fill8, np.uint8),
         "v": np.full(w.num_pages * w.hkv * w.d * PAGE, 0x7FC0 if poison else 0, np.uint16),

@@ -70,12 +70,12 @@ def lib():
         L.ora_pack.argtypes = [P, i, i, P]
         L.ora_unpack.argtypes = [P, i, i, P]
         L.ora_encode.restype = i
-        L.ora_encode.argtypes = [i, i, i, P, P, P, i, P, P, P, P, P, P, i64]
+        L.ora_encode.argtypes = [i, i, i, P, P, P, i, i, P, P, P, P, P, P, i64]
         L.ora_decode.restype = i
-        L.ora_decode.argtypes = [i, i, i, P, P, P, i, P, P, P, P, i, i, P, i, P, d, i,
+        L.ora_decode.argtypes = [i, i, i, P, P, P, i, i, P, P, P, P, i, i, P, i, P, d, i,
                                  P, P, P, i, i]
         L.ora_decoded_keys.restype = i
-        L.ora_decoded_keys.argtypes = [i, i, i, P, P, P, i, P, P, P, i, P]
+        L.ora_decoded_keys.argtypes = [i, i, i, P, P, P, i, i, P, P, P, i, P]
         L.ora_dense_decode.restype = i
         L.ora_dense_decode.argtypes = [i, i, P, P, P, i, i, P, i, P, d, P, P, i]
         L.ora_rdr_plan.restype = i
@@ -189,7 +189,9 @@ def encode(pools: dict, keys, values, slot, radius_mode: int, rng) -> None:
     """Encode keys [n][hkv][d] (and values) into host pools in place.
 
     pools: dict with d, hkv, page_bits (u8[num_pages]), page_off (u64 or None),
-    bstride (int), kcode (u8), rcode (u8[num_pages*hkv*16]), v (u16)."""
+    bstride (int), kcode (u8), rcode (u8[num_pages*hkv*16]), v (u16), and
+    optionally head_tiers (true: page_bits and page_off are per (page, KV
+    head), [num_pages*hkv], the offset of that head's 16 records)."""
     keys = _c(keys, np.float32)
     values = _c(values, np.uint16)
     slot = _c(slot, np.int64)
@@ -197,6 +199,7 @@ def encode(pools: dict, keys, values, slot, radius_mode: int, rng) -> None:
     n = keys.shape[0]
     r = lib().ora_encode(pools["d"], pools["hkv"], radius_mode, _p(rng),
                          _p(pools["page_bits"]), _p(pools.get("page_off")), pools["bstride"],
+                         int(bool(pools.get("head_tiers", False))),
                          _p(pools["kcode"]), _p(pools["rcode"]), _p(pools["v"]),
                          _p(keys), _p(values), _p(slot), n)
     if r:
@@ -220,6 +223,7 @@ def decode(pools: dict, radius_mode: int, rng, q, block_table, seq_lens, scale: 
     npairs = 0 if pr is None else pr.shape[0]
     r = lib().ora_decode(pools["d"], pools["hkv"], radius_mode, _p(rng),
                          _p(pools["page_bits"]), _p(pools.get("page_off")), pools["bstride"],
+                         int(bool(pools.get("head_tiers", False))),
                          _p(pools["kcode"]), _p(pools["rcode"]), _p(pools["v"]),
                          _p(q), B, hq, _p(block_table), max_pages, _p(seq_lens), float(scale),
                          query_mode, _p(out), _p(logits), _p(pr), npairs, int(nthreads))
@@ -236,7 +240,8 @@ def decoded_keys(pools: dict, radius_mode: int, rng, phys):
     d, hkv = pools["d"], pools["hkv"]
     out = np.zeros((phys.shape[0], hkv, PAGE, d), np.float64)
     r = lib().ora_decoded_keys(d, hkv, radius_mode, _p(rng), _p(pools["page_bits"]), _p(pools.get("page_off")),
-                               pools["bstride"], _p(pools["kcode"]), _p(pools["rcode"]), _p(phys),
+                               pools["bstride"], int(bool(pools.get("head_tiers", False))),
+                               _p(pools["kcode"]), _p(pools["rcode"]), _p(phys),
                                phys.shape[0], _p(out))
     if r:
         raise ValueError("ora_decoded_keys: bad page header")

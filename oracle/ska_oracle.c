@@ -351,7 +351,11 @@ void ora_unpack(const uint8_t *rec, int d, int b, int32_t *codes)
  *                             else phys * hkv * 16 * KB(bstride)
  *   rcode[phys][hkv][16]    : radius codes
  *   v[phys][hkv][d][16]     : bf16 values, dimension-major inside a page
- * A slot is phys*16 + token-in-page. */
+ * A slot is phys*16 + token-in-page.
+ * With head_tiers set, the tier is per (page, KV head) instead ([SKV 2.2]
+ * allocates per token, head and layer): page_bits[phys*hkv + g] is the
+ * header of KV head g's 16 records in the page, which start at
+ * kcode + page_off[phys*hkv + g] (page_off required). */
 static size_t page_base(int64_t phys, int hkv, int d, const uint64_t *page_off, int bstride)
 {
     if (page_off)
@@ -359,16 +363,31 @@ static size_t page_base(int64_t phys, int hkv, int d, const uint64_t *page_off, 
     return (size_t)phys * (size_t)hkv * ORA_PAGE * (size_t)ora_kb(d, bstride);
 }
 
+/* tier of KV head g's records in page phys */
+static int tier_of(const uint8_t *page_bits, int head_tiers, int64_t phys, int hkv, int g)
+{
+    return head_tiers ? page_bits[(size_t)phys * hkv + g] : page_bits[phys];
+}
+
+/* byte offset of the record of (page phys, KV head g, slot), kb bytes each */
+static size_t rec_off(int64_t phys, int g, int slot, int kb, int hkv, int d, const uint64_t *page_off,
+                      int bstride, int head_tiers)
+{
+    if (head_tiers)
+        return (size_t)page_off[(size_t)phys * hkv + g] + (size_t)slot * kb;
+    return page_base(phys, hkv, d, page_off, bstride) + ((size_t)g * ORA_PAGE + slot) * kb;
+}
+
 /* Encode keys (and scatter values) into the pools: the step "dense keys ->
  * spherical codes -> compressed store" of [SKV 2.3].  keys [n][hkv][d] fp32,
  * values [n][hkv][d] bf16 bits or NULL, slot[n].  range[hkv][2] = (R_lo, R_hi).
  * Returns 0, or 1 on a bad argument. */
 int ora_encode(int d, int hkv, int radius_mode, const double *range,
-               const uint8_t *page_bits, const uint64_t *page_off, int bstride,
+               const uint8_t *page_bits, const uint64_t *page_off, int bstride, int head_tiers,
                uint8_t *kcode, uint8_t *rcode, uint16_t *v,
                const float *keys, const uint16_t *values, const int64_t *slot, int64_t n)
 {
-    if (d < 8 || d % 4 != 0 || hkv <= 0 || n < 0)
+    if (d < 8 || d % 4 != 0 || hkv <= 0 || n < 0 || (head_tiers && !page_off))
         return 1;
     double *level = malloc(sizeof(double) * 256 * (size_t)hkv);
     double *tau2 = malloc(sizeof(double) * 255 * (size_t)hkv);
@@ -382,14 +401,14 @@ int ora_encode(int d, int hkv, int radius_mode, const double *range,
     for (int64_t i = 0; i < n; ++i) {
         int64_t phys = slot[i] / ORA_PAGE;
         int s = (int)(slot[i] % ORA_PAGE);
-        int b = page_bits[phys];
-        if (b < 1 || b > 8) {
-            bad = 1;
-            continue;
-        }
         int32_t codes[1024];
         uint8_t rec[2048];
         for (int g = 0; g < hkv; ++g) {
+            int b = tier_of(page_bits, head_tiers, phys, hkv, g);
+            if (b < 1 || b > 8) {
+                bad = 1;
+                continue;
+            }
             const float *x = keys + ((size_t)i * hkv + g) * d;
             double S = key_codes_t(x, d, &tab[b], codes);
             if (ora_pack(codes, d, b, rec)) {
@@ -397,7 +416,7 @@ int ora_encode(int d, int hkv, int radius_mode, const double *range,
                 continue;
             }
             int kb = ora_kb(d, b);
-            size_t off = page_base(phys, hkv, d, page_off, bstride) + ((size_t)g * ORA_PAGE + s) * kb;
+            size_t off = rec_off(phys, g, s, kb, hkv, d, page_off, bstride, head_tiers);
             memcpy(kcode + off, rec, (size_t)kb);
             rcode[((size_t)phys * hkv + g) * ORA_PAGE + s] = (uint8_t)ora_radius_code(S, tau2 + 255 * g);
             if (values && v)
@@ -437,13 +456,13 @@ static double bf16_to_double(uint16_t h)
  * units, at logical token positions); pairs = list of (s, h) to compute, or
  * NULL for all.  Returns 0, or 1 on a bad argument. */
 int ora_decode(int d, int hkv, int radius_mode, const double *range,
-               const uint8_t *page_bits, const uint64_t *page_off, int bstride,
+               const uint8_t *page_bits, const uint64_t *page_off, int bstride, int head_tiers,
                const uint8_t *kcode, const uint8_t *rcode, const uint16_t *v,
                const float *q, int B, int hq, const int32_t *block_table, int max_pages,
                const int32_t *seq_lens, double scale, int query_mode,
                float *out, float *logits, const int32_t *pairs, int npairs, int nthreads)
 {
-    if (d < 8 || d % 4 != 0 || hkv <= 0 || hq <= 0 || hq % hkv != 0 || B < 0)
+    if (d < 8 || d % 4 != 0 || hkv <= 0 || hq <= 0 || hq % hkv != 0 || B < 0 || (head_tiers && !page_off))
         return 1;
     if (scale == 0.0)
         scale = 1.0 / sqrt((double)d);
@@ -489,7 +508,7 @@ int ora_decode(int d, int hkv, int radius_mode, const double *range,
         for (int t = 0; t < n; ++t) {
             int64_t phys = block_table[(size_t)s * max_pages + t / ORA_PAGE];
             int slot = t % ORA_PAGE;
-            int b = page_bits[phys];
+            int b = tier_of(page_bits, head_tiers, phys, hkv, g);
             if (b < 1 || b > 8) {
                 bad = 1;
                 b = 1;
@@ -505,7 +524,7 @@ int ora_decode(int d, int hkv, int radius_mode, const double *range,
                 have[b] = 1;
             }
             int kb = ora_kb(d, b);
-            const uint8_t *rec = kcode + page_base(phys, hkv, d, page_off, bstride) + ((size_t)g * ORA_PAGE + slot) * kb;
+            const uint8_t *rec = kcode + rec_off(phys, g, slot, kb, hkv, d, page_off, bstride, head_tiers);
             ora_unpack(rec, d, b, kc);
             ora_direction(kc, d, b, u);
             double r = level[256 * g + rcode[((size_t)phys * hkv + g) * ORA_PAGE + slot]];
@@ -551,25 +570,27 @@ int ora_decode(int d, int hkv, int radius_mode, const double *range,
  * binary64 (page i of phys_list at out + i*hkv*16*d).  Returns 0, or 1 on a
  * bad header. */
 int ora_decoded_keys(int d, int hkv, int radius_mode, const double *range,
-                     const uint8_t *page_bits, const uint64_t *page_off, int bstride,
+                     const uint8_t *page_bits, const uint64_t *page_off, int bstride, int head_tiers,
                      const uint8_t *kcode, const uint8_t *rcode,
                      const int32_t *phys_list, int n, double *out)
 {
+    if (head_tiers && !page_off)
+        return 1;
     int bad = 0;
     int32_t codes[1024];
     double u[1024], level[256], tau2[255];
     for (int i = 0; i < n; ++i) {
         int64_t phys = phys_list[i];
-        int b = page_bits[phys];
-        if (b < 1 || b > 8) {
-            bad = 1;
-            continue;
-        }
-        int kb = ora_kb(d, b);
         for (int g = 0; g < hkv; ++g) {
+            int b = tier_of(page_bits, head_tiers, phys, hkv, g);
+            if (b < 1 || b > 8) {
+                bad = 1;
+                continue;
+            }
+            int kb = ora_kb(d, b);
             ora_radius_tables(radius_mode, range[2 * g], range[2 * g + 1], level, tau2);
             for (int slot = 0; slot < ORA_PAGE; ++slot) {
-                const uint8_t *rec = kcode + page_base(phys, hkv, d, page_off, bstride) + ((size_t)g * ORA_PAGE + slot) * kb;
+                const uint8_t *rec = kcode + rec_off(phys, g, slot, kb, hkv, d, page_off, bstride, head_tiers);
                 ora_unpack(rec, d, b, codes);
                 ora_direction(codes, d, b, u);
                 double r = level[rcode[((size_t)phys * hkv + g) * ORA_PAGE + slot]];
