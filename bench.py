@@ -176,6 +176,8 @@ def main():
                     help="also time ADA and dense bf16 at T = 8K, 32K, 128K with gqa_t32k's batch shape")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the dense-bf16 and decompress-then-dot timings on the same pages")
+    ap.add_argument("--head-tiers", action="store_true",
+                    help="mixed_tiers only: a tier per (page, KV head) instead of per page")
     ap.add_argument("--no-append", action="store_true",
                     help="skip the timing of the decode step with append (ska_append_decode_attention)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle timing")
@@ -193,7 +195,7 @@ def main():
     from long_context_decode_ada_amd import workloads as W
 
     t0 = time.time()
-    w = W.make(args.workload)
+    w = W.make(args.workload, head_tiers=args.head_tiers)
     log("workload %s: B=%d hq=%d hkv=%d d=%d tokens=%d pages=%d (%.1fs)" %
         (w.name, w.B, w.hq, w.hkv, w.d, w.n_tokens, w.num_pages, time.time() - t0))
     dev = "cuda"
@@ -377,7 +379,8 @@ def main():
         "kv_tokens_per_s": round(w.n_tokens / (ms_per_step * 1e-3), 1),
         "token_kvhead_per_s": round(w.n_tokens * w.hkv / (ms_per_step * 1e-3), 1),
         "alg_bytes_per_step": int(step_bytes),
-        "config": {"workload": w.name, "B": w.B, "hq": w.hq, "hkv": w.hkv, "d": w.d,
+        "config": {"workload": w.name + (" (tier per page and KV head)" if w.head_tiers else ""),
+                   "B": w.B, "hq": w.hq, "hkv": w.hkv, "d": w.d,
                    "T": int(w.seq_lens.max()), "angle_bits": tiers, "radius": "8-bit " +
                    ("log" if w.radius_mode == W.LOG else "uniform"), "page": 16,
                    "values": "bf16", "pool_copies": nc, "splits": args.splits or "auto"},

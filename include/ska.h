@@ -97,6 +97,11 @@ typedef struct {
     uint8_t *rcode;           /* device: [num_pages][Hkv][16] */
     uint16_t *v;              /* device: bf16 [num_pages][Hkv][d][16] */
     const uint8_t *page_bits; /* device: [num_pages] */
+    int head_tiers;           /* 0: one tier per page (page_bits, page_off as above);
+                                 1: one tier per (page, KV head) (section 2.2 allocates per
+                                 token, head and layer): page_bits [num_pages][Hkv] holds
+                                 the header of each KV head's 16 records and page_off
+                                 (required) [num_pages][Hkv] their byte offset */
 } ska_pool_desc;
 
 /* ska_encode_keys -- the write path of section 2.3: map dense keys to

@@ -63,7 +63,7 @@ __device__ void encode_one(const EncodeArgs &A, const float *__restrict__ x, con
         atomicOr(A.err, 1u);
         return;
     }
-    const int b = A.page_bits[phys];
+    const int b = A.page_bits[A.head_tiers ? phys * A.hkv + g : phys];
     if (b < 1 || b > 8 || !((A.tier_mask >> b) & 1u)) {
         atomicOr(A.err, 4u);
         return;
@@ -90,8 +90,10 @@ __device__ void encode_one(const EncodeArgs &A, const float *__restrict__ x, con
     const int kb = record_bytes(d, b);
     const int sb = kb / 4;          // slice bytes
     const int na = d / 4;           // angles per slice
-    const uint64_t base = A.page_off ? A.page_off[phys] : (uint64_t)phys * (uint64_t)A.page_stride;
-    uint32_t *rec = reinterpret_cast<uint32_t *>(A.kcode + base + ((uint64_t)g * kPage + s) * kb);
+    uint64_t base;
+    if (A.head_tiers) base = A.page_off[phys * A.hkv + g] + (uint64_t)s * kb;
+    else base = (A.page_off ? A.page_off[phys] : (uint64_t)phys * (uint64_t)A.page_stride) + ((uint64_t)g * kPage + s) * kb;
+    uint32_t *rec = reinterpret_cast<uint32_t *>(A.kcode + base);
     for (int sl = 0; sl < 4; ++sl) {
         uint32_t *w = rec + sl * (sb / 4);
         uint64_t acc = 0;

@@ -337,7 +337,9 @@ __device__ __forceinline__ void load_page_any(const DecodeArgs &A, const PageDes
     const int KB = record_bytes(D, pd.b);
     const int64_t pk = (int64_t)pd.phys * A.hkv + kvh;
     const int lv = __builtin_amdgcn_readfirstlane(pd.live ? 1 : 0);
-    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(A.kcode + pd.off + (uint64_t)kvh * kPage * KB, lv * kPage * KB);
+    // (per-(page, KV head) tiers: pd.off is already this head's records)
+    const __amdgpu_buffer_rsrc_t rk =
+        buf_rsrc(A.kcode + pd.off + (A.head_tiers ? 0 : (uint64_t)kvh * kPage * KB), lv * kPage * KB);
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(A.v + pk * (int64_t)D * kPage, lv * D * kPage * 2);
     const __amdgpu_buffer_rsrc_t rr = buf_rsrc(A.rcode + pk * kPage, lv * kPage);
     const int vo = t * KB + j * (KB / 4);
@@ -638,13 +640,14 @@ __device__ __forceinline__ void append_token(const DecodeArgs &A, int seq, int k
     const int pos = len_in - 1, s = pos % kPage;
     // (the header is read now and checked before the stores; with a single
     // tier the codes need not wait for it)
-    const int hb = A.page_bits[ph];
+    const int64_t hix = A.head_tiers ? (int64_t)ph * A.hkv + kvh : (int64_t)ph;
+    const int hb = A.page_bits[hix];
     const int b = TB != 0 ? TB : hb;
     if (TB == 0 && !(b >= 2 && b <= 8 && ((A.tier_mask >> b) & 1u))) {
         if (lane == 0) atomicOr(A.err, 4u);
         return;
     }
-    const uint64_t off = (TB == 0 && A.page_off) ? A.page_off[ph] : (uint64_t)ph * (uint64_t)A.page_stride;
+    const uint64_t off = (TB == 0 && A.page_off) ? A.page_off[hix] : (uint64_t)ph * (uint64_t)A.page_stride;
     if (lane == 0) {
         double T = add_square(0.0, xk[D - 1]);
         T = add_square(T, xk[D - 2]);
@@ -686,8 +689,8 @@ __device__ __forceinline__ void append_token(const DecodeArgs &A, int seq, int k
     // of a slice is bits [32 wi, 32 wi + 32) of that string
     const int kb = record_bytes(D, b), wps = kb / 16;
     constexpr int na = D / 4;
-    uint32_t *rec = reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(A.kcode) + off +
-                                                 ((uint64_t)kvh * kPage + s) * kb);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(
+        const_cast<uint8_t *>(A.kcode) + off + (A.head_tiers ? (uint64_t)s * kb : ((uint64_t)kvh * kPage + s) * kb));
     for (int wq = lane; wq < 4 * wps; wq += 64) {
         const int sl = wq / wps, bit0 = 32 * (wq % wps);
         const int a0 = sl * na, a1 = min((sl + 1) * na, D - 1);
@@ -878,10 +881,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             e_phys = ok ? ph : -1;
             key = ok ? TB : 15;
         } else {
-            // header and offset of the page, read at a clamped (valid) id
+            // header and offset of the page (of this KV head's records with
+            // per-head tiers), read at a clamped (valid) id
             const int phc = ok ? ph : 0;
-            const int bb = (int)A.page_bits[phc];
-            const uint64_t off = A.page_off ? A.page_off[phc] : (uint64_t)phc * (uint64_t)A.page_stride;
+            const int64_t hix = A.head_tiers ? (int64_t)phc * A.hkv + kvh : (int64_t)phc;
+            const int bb = (int)A.page_bits[hix];
+            const uint64_t off = A.page_off ? A.page_off[hix] : (uint64_t)phc * (uint64_t)A.page_stride;
             const bool okb = ok && bb >= 2 && bb <= 8 && ((A.tier_mask >> bb) & 1u);
             if (ok && !okb) atomicOr(A.err, 4u);
             e_phys = okb ? ph : -1;
@@ -1442,8 +1447,9 @@ __global__ __launch_bounds__(kThreads) void k_decompress(DecodeArgs A) {
     if (lane < cnt) {
         btv = A.block_table[(int64_t)seq * A.max_pages + p0 + kWaves * lane];
         if (TB == 0 && (uint32_t)btv < npg32) {
-            hbv = A.page_bits[btv];
-            offv = A.page_off ? A.page_off[btv] : (uint64_t)btv * (uint64_t)A.page_stride;
+            const int64_t hix = A.head_tiers ? (int64_t)btv * A.hkv + kvh : (int64_t)btv;
+            hbv = A.page_bits[hix];
+            offv = A.page_off ? A.page_off[hix] : (uint64_t)btv * (uint64_t)A.page_stride;
         }
     }
     uint32_t err = 0;
@@ -1475,7 +1481,8 @@ __global__ __launch_bounds__(kThreads) void k_decompress(DecodeArgs A) {
         // (the bases are read back as scalars: without that the compiler
         // may form a 64-bit sum on the vector unit and then loop over lanes
         // to build the descriptor)
-        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(scalar_ptr(A.kcode + off + (uint64_t)kvh * kPage * KB),
+        const uint64_t hoff = (TB == 0 && A.head_tiers) ? 0 : (uint64_t)kvh * kPage * KB;
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(scalar_ptr(A.kcode + off + hoff),
                                                    __builtin_amdgcn_readfirstlane(live ? kPage * KB : 0));
         const __amdgpu_buffer_rsrc_t rr = buf_rsrc(scalar_ptr(A.rcode + ((int64_t)phc * A.hkv + kvh) * kPage),
                                                    __builtin_amdgcn_readfirstlane(live ? kPage : 0));

@@ -68,13 +68,15 @@ ska_status check_pool(const ska_pool_desc *p) {
     if (!tiers_ok(p->tier_mask)) return SKA_ERR_INVALID;
     if (p->query_mode != SKA_Q_CODED && p->query_mode != SKA_Q_EXACT) return SKA_ERR_INVALID;
     if (!p->kcode || !p->rcode || !p->v || !p->page_bits) return SKA_ERR_INVALID;
+    if (p->head_tiers != 0 && p->head_tiers != 1) return SKA_ERR_INVALID;
+    if (p->head_tiers && !p->page_off) return SKA_ERR_INVALID;
     return SKA_OK;
 }
 
 bool same_shape(const ska_pool_desc &a, const ska_pool_desc &b) {
     return a.d == b.d && a.num_kv_heads == b.num_kv_heads && a.page_size == b.page_size &&
            a.num_pages == b.num_pages && a.radius_mode == b.radius_mode && a.radius_bits == b.radius_bits &&
-           a.tier_mask == b.tier_mask && a.query_mode == b.query_mode;
+           a.tier_mask == b.tier_mask && a.query_mode == b.query_mode && a.head_tiers == b.head_tiers;
 }
 
 // cos^2, sin^2 of the bin edges j*pi/2^b for b = 1..8 at offset 2^b - 2.
@@ -307,6 +309,7 @@ EncodeArgs encode_args(const ska_cache *c) {
     a.page_bits = c->pool.page_bits;
     a.page_off = c->pool.page_off;
     a.page_stride = c->page_stride;
+    a.head_tiers = c->pool.head_tiers;
     a.kcode = c->pool.kcode;
     a.rcode = c->pool.rcode;
     a.v = c->pool.v;
@@ -452,6 +455,7 @@ ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, in
     da.tier_mask = c->pool.tier_mask;
     da.nt = c->nt;
     for (int b = 0; b <= 8; ++b) da.tslot[b] = c->tslot[b];
+    da.head_tiers = c->pool.head_tiers;
     da.app_k = app_k;
     da.app_v = app_v;
     da.tau2 = c->d_tau2;
@@ -563,6 +567,7 @@ ska_status ska_decompress_keys(ska_cache *c, const int32_t *block_table, int bat
     da.hkv = c->pool.num_kv_heads;
     da.max_pages = max_pages;
     da.tier_mask = c->pool.tier_mask;
+    da.head_tiers = c->pool.head_tiers;
     if (launch_decompress(da, c->pool.d, batch, (hipStream_t)stream) != hipSuccess) return SKA_ERR_HIP;
     return SKA_OK;
 }

@@ -69,6 +69,7 @@ struct EncodeArgs {
     const uint8_t *page_bits;
     const uint64_t *page_off;
     int64_t page_stride;     // bytes per physical page when page_off == NULL
+    int head_tiers;          // page_bits/page_off per (page, KV head): [num_pages][hkv]
     uint8_t *kcode;
     uint8_t *rcode;
     uint16_t *v;
@@ -114,6 +115,10 @@ struct DecodeArgs {
     const float *app_k;      // [B][hkv][d]
     const uint16_t *app_v;   // [B][hkv][d] bf16
     const double *tau2;      // [hkv][255] squared radius edges
+    // page_bits and page_off per (page, KV head), [num_pages][hkv]; the offset
+    // is that head's first record (with per-page tiers: the page's, to which
+    // the head's 16 records at their tier are added)
+    int head_tiers;
 };
 
 

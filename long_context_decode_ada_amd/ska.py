@@ -48,6 +48,7 @@ class PoolDesc(ctypes.Structure):
         ("rcode", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
         ("page_bits", ctypes.c_void_p),
+        ("head_tiers", ctypes.c_int),
     ]
 
 
@@ -113,8 +114,9 @@ class DevicePools:
 
     def __init__(self, *, d: int, hkv: int, num_pages: int, tier_mask: int, radius_mode: int,
                  page_bits: torch.Tensor, kcode_bytes: int, page_off: Optional[torch.Tensor] = None,
-                 query_mode: int = Q_CODED, device="cuda", poison: bool = True):
+                 query_mode: int = Q_CODED, device="cuda", poison: bool = True, head_tiers: bool = False):
         self.d, self.hkv, self.num_pages = d, hkv, num_pages
+        self.head_tiers = bool(head_tiers)
         self.tier_mask, self.radius_mode, self.query_mode = tier_mask, radius_mode, query_mode
         self.page_bits = page_bits.to(device=device, dtype=torch.uint8).contiguous()
         self.page_off = None if page_off is None else page_off.to(device=device, dtype=torch.int64).contiguous()
@@ -129,13 +131,14 @@ class DevicePools:
         off = None if w.page_off is None else torch.from_numpy(w.page_off.view(np.int64))
         return cls(d=w.d, hkv=w.hkv, num_pages=w.num_pages, tier_mask=w.tier_mask, radius_mode=w.radius_mode,
                    page_bits=torch.from_numpy(w.page_bits), kcode_bytes=w.kcode_bytes, page_off=off,
-                   query_mode=query_mode, device=device, poison=poison)
+                   query_mode=query_mode, device=device, poison=poison, head_tiers=w.head_tiers)
 
     def desc(self) -> PoolDesc:
         return PoolDesc(self.d, self.hkv, PAGE, self.num_pages, self.radius_mode, 8, self.tier_mask,
                         self.query_mode, self.kcode.data_ptr(),
                         None if self.page_off is None else self.page_off.data_ptr(),
-                        self.rcode.data_ptr(), self.v.data_ptr(), self.page_bits.data_ptr())
+                        self.rcode.data_ptr(), self.v.data_ptr(), self.page_bits.data_ptr(),
+                        int(self.head_tiers))
 
     def to_host(self) -> dict:
         return {"kcode": self.kcode.cpu().numpy(), "rcode": self.rcode.cpu().numpy(),

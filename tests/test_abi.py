@@ -33,7 +33,8 @@ def test_status_strings():
 
 def _desc(**kw):
     base = dict(d=128, num_kv_heads=8, page_size=16, num_pages=4, radius_mode=1, radius_bits=8,
-                tier_mask=1 << 4, query_mode=0, kcode=16, page_off=None, rcode=16, v=16, page_bits=16)
+                tier_mask=1 << 4, query_mode=0, kcode=16, page_off=None, rcode=16, v=16, page_bits=16,
+                head_tiers=0)
     base.update(kw)
     return ska.PoolDesc(*[base[f] for f, _ in ska.PoolDesc._fields_])
 
@@ -58,6 +59,8 @@ def _enc(desc, n=1, keys=16, slot=16, rr=None, cache=None):
     (dict(kcode=None), ska.SKA_ERR_INVALID),
     (dict(v=None), ska.SKA_ERR_INVALID),
     (dict(page_bits=None), ska.SKA_ERR_INVALID),
+    (dict(head_tiers=2), ska.SKA_ERR_INVALID),
+    (dict(head_tiers=1), ska.SKA_ERR_INVALID),          # per-head tiers need the offsets
 ])
 def test_encode_rejects_bad_pool(kw, expect):
     assert _enc(_desc(**kw)) == expect
