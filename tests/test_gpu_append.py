@@ -160,3 +160,30 @@ def test_append_edges_empty_row_and_out_of_row():
     snap2 = pools.to_host()
     for k in ("kcode", "rcode", "v"):
         assert np.array_equal(snap[k], snap2[k]), k
+
+
+def test_append_at_full_size_gqa_t32k():
+    """The benchmark's configuration (8 x 32K tokens, automatic splits, the
+    production kernel): every sequence's last token appended by the step;
+    every pool byte and every output compared with the oracle."""
+    import time
+    from long_context_decode_ada_amd import ska
+    t0 = time.time()
+    w = W.make("gqa_t32k")
+    rng = O.calibrate(w.keys)
+    lens = w.seq_lens.astype(np.int64)
+    say("[append full] generated (%.1fs)" % (time.time() - t0))
+    pools, cache, rows = _setup(w, rng, lens - 1)
+    g = _step(w, cache, rows, lens, want_logits=False)
+    assert ska.device_errors(cache) == 0
+    say("[append full] GPU done (%.1fs)" % (time.time() - t0))
+    o = oracle_run(w, rng, want_logits=False)
+    say("[append full] oracle done (%.1fs)" % (time.time() - t0))
+    host = pools.to_host()
+    for k in ("kcode", "rcode", "v"):
+        nd = int(np.count_nonzero(host[k] != o["pools"][k]))
+        say("[append full] %s mismatching bytes: %d" % (k, nd))
+        assert nd == 0
+    err = float(np.abs(g["out"] - o["out"]).max())
+    say("[append full] max|out err| %.3g" % err)
+    assert err <= 2e-3

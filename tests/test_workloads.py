@@ -66,3 +66,17 @@ def test_small_workloads_run_through_the_oracle():
         O.encode(pools, w.keys, w.values, w.slot, w.radius_mode, rg)
         out = O.decode(pools, w.radius_mode, rg, w.q, w.block_table, w.seq_lens)
         assert np.isfinite(out).all()
+
+
+def test_head_tier_layout_is_packed_per_page_and_head():
+    w = W.make("mixed_tiers", 1 / 64, batch=2, head_tiers=True)
+    assert w.page_bits.shape == (w.num_pages * w.hkv,) and w.page_off.shape == (w.num_pages * w.hkv,)
+    sizes = W.PAGE * np.array([W.record_bytes(w.d, int(b)) for b in w.page_bits], np.uint64)
+    assert w.page_off[0] == 0 and np.array_equal(np.diff(w.page_off), sizes[:-1])
+    assert w.kcode_bytes == int(sizes.sum())
+    hb = w.page_bits.reshape(w.num_pages, w.hkv)
+    assert set(np.unique(hb)) <= {2, 4, 6, 8}
+    for s in range(w.B):                      # the sink page: every head at the widest tier
+        assert (hb[w.block_table[s, 0]] == 8).all()
+    w0 = W.make("mixed_tiers", 1 / 64, batch=2)
+    assert np.array_equal(w0.seq_lens, w.seq_lens) and np.array_equal(w0.block_table, w.block_table)
