@@ -185,7 +185,7 @@ def main():
                     help="also run a plain copy kernel of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the decode needs no inter-GPU "
+        print("bench.py: this benchmark measures one GPU only (the decode needs no inter-GPU "
               "communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
