@@ -234,8 +234,13 @@ typedef struct {
  *   status_out int32 [batch]: 0, or 2 when the protected states alone exceed
  *              the budget (they are kept and every other state is evicted)
  * Decisions are binary64 comparisons made as written (no contraction), so
- * the plan is reproducible bit for bit.  Returns SKA_OK, SKA_ERR_INVALID on
- * a bad parameter or size. */
+ * the plan is reproducible bit for bit.  The library keeps a device
+ * workspace for this call per device (allocated on first use, about
+ * batch * (2.5 KB + 16 B per 512 states); growing it synchronises the
+ * device); calls that overlap on one device must not run concurrently.
+ * Returns SKA_OK, SKA_ERR_INVALID on a bad parameter or size,
+ * SKA_ERR_UNSUPPORTED for batch > 65535, SKA_ERR_HIP if the workspace
+ * cannot be allocated. */
 ska_status ska_rdr_plan(const ska_rdr_params *params, const float *utility, const float *key_norm,
                         const uint8_t *protect, const int32_t *num_states, const int64_t *budget, int batch,
                         int max_states, uint8_t *tier_out, int32_t *page_out, int32_t *slot_out,

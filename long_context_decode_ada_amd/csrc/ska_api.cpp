@@ -501,6 +501,38 @@ ska_status ska_dense_decode_attention(ska_cache *c, const uint16_t *k_dense, con
                        out, logits_dbg, stream);
 }
 
+namespace {
+
+// The RDR workspace of the current device: allocated on first use, grown
+// (after a device synchronisation, so that no call in flight still uses the
+// old one) when a call needs more, kept until the process ends.
+struct RdrWorkspace {
+    void *p = nullptr;
+    size_t n = 0;
+};
+RdrWorkspace g_rdr_ws[64];
+
+ska_status rdr_workspace(size_t bytes, char **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SKA_ERR_HIP;
+    RdrWorkspace &w = g_rdr_ws[dev];
+    if (w.n < bytes) {
+        if (w.p) {
+            if (hipDeviceSynchronize() != hipSuccess) return SKA_ERR_HIP;
+            (void)hipFree(w.p);
+            w.p = nullptr;
+            w.n = 0;
+        }
+        const size_t want = std::max(bytes, (size_t)1 << 20);
+        if (hipMalloc(&w.p, want) != hipSuccess) return SKA_ERR_HIP;
+        w.n = want;
+    }
+    *out = static_cast<char *>(w.p);
+    return SKA_OK;
+}
+
+}  // namespace
+
 ska_status ska_rdr_plan(const ska_rdr_params *p, const float *utility, const float *key_norm,
                         const uint8_t *protect, const int32_t *num_states, const int64_t *budget, int batch,
                         int max_states, uint8_t *tier_out, int32_t *page_out, int32_t *slot_out,
@@ -516,6 +548,7 @@ ska_status ska_rdr_plan(const ska_rdr_params *p, const float *utility, const flo
     }
     if (max_pages_out < (max_states + 15) / 16 + p->ntiers) return SKA_ERR_INVALID;
     if (batch == 0) return SKA_OK;
+    if (batch > 65535) return SKA_ERR_UNSUPPORTED;   // the sequence is the grid's y dimension
     if (!utility || !key_norm || !protect || !num_states || !budget || !tier_out || !page_out || !slot_out ||
         !page_tier_out || !npages_out || !lambda_out || !status_out)
         return SKA_ERR_INVALID;
@@ -541,7 +574,21 @@ ska_status ska_rdr_plan(const ska_rdr_params *p, const float *utility, const flo
     a.npages = npages_out;
     a.lambda = lambda_out;
     a.status = status_out;
-    if (launch_rdr(a, batch, (hipStream_t)stream) != hipSuccess) return SKA_ERR_HIP;
+    // workspace (bound, per-round totals and intervals, per-chunk tier
+    // counts), kept per device and grown when a call needs more
+    hipStream_t s = (hipStream_t)stream;
+    a.nchunk = std::max(1, (max_states + rdr_chunk_states() - 1) / rdr_chunk_states());
+    const size_t n_hib = (size_t)batch, n_tot = (size_t)batch * 17 * 16, n_iv = (size_t)batch * 17 * 2;
+    const size_t n_cnt = (size_t)batch * a.nchunk * 8;
+    const size_t off_tot = n_hib * 8, off_iv = off_tot + n_tot * 8, off_cnt = off_iv + n_iv * 8;
+    char *ws = nullptr;
+    if (rdr_workspace(off_cnt + n_cnt * 4, &ws) != SKA_OK) return SKA_ERR_HIP;
+    a.ws_hib = reinterpret_cast<unsigned long long *>(ws);
+    a.ws_tot = reinterpret_cast<long long *>(ws + off_tot);
+    a.ws_iv = reinterpret_cast<double *>(ws + off_iv);
+    a.ws_cnt = reinterpret_cast<int32_t *>(ws + off_cnt);
+    if (launch_zero_u32(reinterpret_cast<uint32_t *>(ws), (int64_t)(off_iv / 4), s) != hipSuccess) return SKA_ERR_HIP;
+    if (launch_rdr(a, batch, s) != hipSuccess) return SKA_ERR_HIP;
     return SKA_OK;
 }
 

@@ -27,8 +27,17 @@ struct RdrArgs {
     int32_t *npages;         // [B]
     double *lambda;          // [B] the multiplier of the plan
     int32_t *status;         // [B] 0, or 2: protected states alone over the budget
+    // workspace: per sequence the bound's bit pattern, the byte totals of each
+    // round ([17][16]), the interval of each round ([17][2]) and per chunk the
+    // count of each tier ([nchunk][8]); ws_hib and ws_tot zero on entry
+    unsigned long long *ws_hib;   // [B]
+    long long *ws_tot;            // [B][17][16]
+    double *ws_iv;                // [B][17][2]
+    int32_t *ws_cnt;              // [B][nchunk][8]
+    int nchunk;                   // chunks of rdr_chunk_states() states per sequence
 };
 
 hipError_t launch_rdr(const RdrArgs &a, int batch, hipStream_t s);
+int rdr_chunk_states();
 
 }  // namespace ska
