@@ -236,7 +236,7 @@ typedef struct {
  * Decisions are binary64 comparisons made as written (no contraction), so
  * the plan is reproducible bit for bit.  The library keeps a device
  * workspace for this call per device (allocated on first use, about
- * batch * (2.5 KB + 16 B per 512 states); growing it synchronises the
+ * batch * (2.5 KB + 32 B per 512 states), at least 1 MiB; growing it synchronises the
  * device); calls that overlap on one device must not run concurrently.
  * Returns SKA_OK, SKA_ERR_INVALID on a bad parameter or size,
  * SKA_ERR_UNSUPPORTED for batch > 65535, SKA_ERR_HIP if the workspace

@@ -167,3 +167,30 @@ def test_rdr_plan_drives_the_coded_decode():
     for k in ("kcode", "rcode", "v"):
         assert np.array_equal(gr["pools"][k], orr["pools"][k]), k
     compare(w2, gr, orr, rng_r, label="rdr pages")
+
+
+def test_many_sequences_after_a_small_call():
+    """A small call, then one whose workspace outgrows the first (512
+    sequences): every plan still equals the oracle's (a sample of rows
+    checked in full)."""
+    rng = np.random.default_rng(23)
+    u = rng.exponential(1.0, (2, 300)).astype(np.float32)
+    kn = rng.uniform(3.0, 40.0, (2, 300)).astype(np.float32)
+    _gpu_plan(u, kn, np.zeros((2, 300), np.uint8), np.array([300, 120], np.int32),
+              np.array([50000, 20000], np.int64), 0.04)
+    B, T = 512, 1100
+    u = rng.exponential(1.0, (B, T)).astype(np.float32)
+    kn = rng.uniform(3.0, 40.0, (B, T)).astype(np.float32)
+    prot = np.zeros((B, T), np.uint8)
+    prot[:, :2] = 1
+    lens = rng.integers(0, T + 1, B).astype(np.int32)
+    budget = (rng.uniform(0.05, 1.0, B) * lens * BYTES[-1]).astype(np.int64)
+    g = _gpu_plan(u, kn, prot, lens, budget, 0.04)
+    for s in list(range(0, B, 37)) + [B - 1]:
+        n = int(lens[s])
+        o = O.rdr_plan(u[s, :n], kn[s, :n], prot[s, :n], TIERS, EPS, BYTES, int(budget[s]), 0.04)
+        assert g["status"][s] == o["status"] and g["lambda"][s] == o["lambda"], s
+        assert g["npages"][s] == len(o["page_tier"]), s
+        assert np.array_equal(g["tier"][s, :n], o["tier"]), s
+        assert np.array_equal(g["page"][s, :n], o["page"]), s
+        assert np.array_equal(g["slot"][s, :n], o["slot"]), s
