@@ -98,6 +98,28 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_BF16_BITS = (torch.int16, torch.uint16, torch.bfloat16) if hasattr(torch, "uint16") else (torch.int16, torch.bfloat16)
+
+
+def _dev(name: str, t: Optional[torch.Tensor], dtypes, shape=None, optional: bool = False):
+    """The C ABI takes raw device pointers, so a tensor of the wrong dtype,
+    device, layout or shape would be read as garbage: refuse it here."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s: a tensor is required" % name)
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if not t.is_cuda:
+        raise ValueError("%s: must be a device tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s: dtype %s, expected %s" % (name, t.dtype, " or ".join(str(d) for d in dtypes)))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -169,6 +191,11 @@ def encode_keys(cache: Cache, keys: torch.Tensor, values: Optional[torch.Tensor]
     """ska_encode_keys: keys fp32 [n][hkv][d], values bf16 bits (int16/uint16/bf16) [n][hkv][d] or
     None, slot int64 [n], radius_range host [hkv][2] or None."""
     n = int(keys.shape[0]) if keys is not None else 0
+    P = cache.pools
+    if n > 0:
+        _dev("keys", keys, torch.float32, (n, P.hkv, P.d))
+        _dev("values", values, _BF16_BITS, (n, P.hkv, P.d), optional=True)
+        _dev("slot", slot, torch.int64, (n,))
     desc = cache.pools.desc()
     rr = None
     if radius_range is not None:
@@ -180,12 +207,27 @@ def encode_keys(cache: Cache, keys: torch.Tensor, values: Optional[torch.Tensor]
     return cache
 
 
+def _decode_checks(cache, q, block_table, seq_lens, out, logits):
+    P = cache.pools
+    if q.dim() != 3 or q.shape[2] != P.d:
+        raise ValueError("q: shape %s, expected [B][Hq][%d]" % (tuple(q.shape), P.d))
+    B, hq, d = q.shape
+    _dev("q", q, torch.float32)
+    _dev("block_table", block_table, torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table: shape %s, expected [%d][max_pages]" % (tuple(block_table.shape), B))
+    _dev("seq_lens", seq_lens, torch.int32, (B,))
+    _dev("out", out, torch.float32, (B, hq, d), optional=True)
+    _dev("logits", logits, torch.float32, (B, hq, block_table.shape[1] * PAGE), optional=True)
+
+
 def decode_attention(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                      scale: float = 0.0, num_splits: int = 0, out: Optional[torch.Tensor] = None,
                      logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """ska_decode_attention: q fp32 [B][hq][d], block_table int32 [B][max_pages], seq_lens int32 [B];
     returns out fp32 [B][hq][d].  logits (fp32 [B][hq][max_pages*16]) is filled if given."""
     B, hq, d = q.shape
+    _decode_checks(cache, q, block_table, seq_lens, out, logits)
     if out is None:
         out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
     s = lib().ska_decode_attention(cache.handle, _ptr(q), B, hq, _ptr(block_table), int(block_table.shape[1]),
@@ -203,6 +245,9 @@ def append_decode_attention(cache: Cache, new_keys: torch.Tensor, new_values: to
     view) are stored at position seq_lens[s]-1 of each sequence (seq_lens include them), then the decode
     as decode_attention."""
     B, hq, d = q.shape
+    _decode_checks(cache, q, block_table, seq_lens, out, logits)
+    _dev("new_keys", new_keys, torch.float32, (B, cache.pools.hkv, cache.pools.d))
+    _dev("new_values", new_values, _BF16_BITS, (B, cache.pools.hkv, cache.pools.d))
     if out is None:
         out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
     s = lib().ska_append_decode_attention(cache.handle, _ptr(new_keys), _ptr(new_values), _ptr(q), B, hq,
@@ -219,6 +264,9 @@ def dense_decode_attention(cache: Cache, k_dense: torch.Tensor, q: torch.Tensor,
     """ska_dense_decode_attention: keys bf16 bits k_dense [num_pages][hkv][16][d] (int16/uint16 view),
     the cache's values; otherwise as decode_attention."""
     B, hq, d = q.shape
+    _decode_checks(cache, q, block_table, seq_lens, out, logits)
+    P = cache.pools
+    _dev("k_dense", k_dense, _BF16_BITS, (P.num_pages, P.hkv, PAGE, P.d))
     if out is None:
         out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
     s = lib().ska_dense_decode_attention(cache.handle, _ptr(k_dense), _ptr(q), B, hq, _ptr(block_table),
@@ -231,6 +279,11 @@ def dense_decode_attention(cache: Cache, k_dense: torch.Tensor, q: torch.Tensor,
 def decompress_keys(cache: Cache, block_table: torch.Tensor, seq_lens: torch.Tensor, k_dense: torch.Tensor,
                     stream=None) -> torch.Tensor:
     """ska_decompress_keys: writes bf16 r~ u(c) of the resident pages into k_dense [num_pages][hkv][16][d]."""
+    P = cache.pools
+    B = int(block_table.shape[0])
+    _dev("block_table", block_table, torch.int32)
+    _dev("seq_lens", seq_lens, torch.int32, (B,))
+    _dev("k_dense", k_dense, _BF16_BITS, (P.num_pages, P.hkv, PAGE, P.d))
     s = lib().ska_decompress_keys(cache.handle, _ptr(block_table), int(block_table.shape[0]),
                                   int(block_table.shape[1]), _ptr(seq_lens), _ptr(k_dense), _stream(stream))
     _check(s, "ska_decompress_keys")
@@ -248,6 +301,11 @@ def rdr_plan(utility: torch.Tensor, key_norm: torch.Tensor, protect: torch.Tenso
     budget int64 [B].  Returns dict of device tensors tier (uint8), page, slot (int32) [B][T],
     page_tier (uint8) [B][P], npages (int32), lambda (float64), status (int32) [B]."""
     B, T = utility.shape
+    _dev("utility", utility, torch.float32, (B, T))
+    _dev("key_norm", key_norm, torch.float32, (B, T))
+    _dev("protect", protect, torch.uint8, (B, T))
+    _dev("num_states", num_states, torch.int32, (B,))
+    _dev("budget", budget, torch.int64, (B,))
     p = RdrParams()
     p.ntiers = len(tiers)
     for k in range(len(tiers)):

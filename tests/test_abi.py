@@ -106,3 +106,21 @@ def test_baseline_entry_points_reject_bad_arguments_without_a_cache():
     L = ska.lib()
     assert L.ska_dense_decode_attention(None, 16, 16, 1, 32, 16, 4, 16, 0.0, 0, 16, None, None) == ska.SKA_ERR_INVALID
     assert L.ska_decompress_keys(None, 16, 1, 4, 16, 16, None) == ska.SKA_ERR_INVALID
+
+
+def test_binding_refuses_tensors_it_cannot_pass_through():
+    """The binding checks dtype, device, layout and shape before any call:
+    the C ABI would read a wrong tensor as garbage."""
+    import types
+    import torch
+    fake = types.SimpleNamespace(pools=types.SimpleNamespace(d=64, hkv=1, num_pages=4), handle=None)
+    q = torch.zeros((2, 1, 64))
+    bt = torch.zeros((2, 4), dtype=torch.int32)
+    sl = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device"):
+        ska.decode_attention(fake, q, bt, sl)
+    with pytest.raises(ValueError, match="shape"):
+        ska.decode_attention(fake, torch.zeros((2, 1, 32)), bt, sl)
+    with pytest.raises(ValueError):
+        ska.rdr_plan(torch.zeros((2, 8)), torch.zeros((2, 8)), torch.zeros((2, 8), dtype=torch.uint8),
+                     torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int64), [4], [0.1], [100], 0.1)
