@@ -714,18 +714,79 @@ __device__ __forceinline__ void append_token(const DecodeArgs &A, int seq, int k
 // TB: the angle bit width of every page when the pool has a single tier, or 0
 // (pages of mixed tiers, dispatched per page on the header).  APP: the decode
 // step with append (append_token).
+// The split layout of a sequence's pages: split j starts at page
+// split_start(j).  With b = pps and m = split_m the sizes are b, b, 2b, 4b,
+// ..., b 2^m, then b 2^m each; m = 0 gives splits of b pages throughout.
+__device__ __forceinline__ int split_start(const DecodeArgs &A, int j) {
+    const int m = A.split_m;
+    if (j <= m + 1) return j == 0 ? 0 : A.pps << (j - 1);
+    return (j - m) * (A.pps << m);
+}
+// number of splits that hold pages of a sequence of n pages
+__device__ __forceinline__ int splits_of(const DecodeArgs &A, int n) {
+    if (n <= 0) return 0;
+    const int m = A.split_m, cap = A.pps << m;
+    if (n > cap) return m + (n + cap - 1) / cap;
+    int k = 1;
+    while (k <= m + 1 && (A.pps << (k - 1)) < n) ++k;
+    return k;
+}
+
 template <int D, int G, int TB, bool DBG, bool APP = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void k_decode(DecodeArgs A) {
     constexpr int NA = D / 4;
     constexpr int NT = D / 16;
     // The split is the slowest grid dimension, taken in reverse: the
-    // dispatcher hands out the last split of every group first.  Only long
-    // sequences have work in the high splits (the workgroups past the end of
-    // a short one exit at once), so in a ragged batch the longest sequences
-    // start first and the short ones fill CUs as they free up (ragged_b64:
-    // 455 -> 444 us; uniform batches are unaffected).
-    const int kvh = blockIdx.x, seq = blockIdx.y, split = (int)gridDim.z - 1 - (int)blockIdx.z;
+    // dispatcher hands out the last split of every group first, so in a
+    // batch of one round the longest sequences start first.  In a batch of
+    // several rounds the splits grow with their index (split_start) and the
+    // grid is compacted, so the largest units go first and the smallest
+    // fill the last round.
+    const int kvh = blockIdx.x;
+    int seq = blockIdx.y, split = (int)gridDim.z - 1 - (int)blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
+    int len_known = 0;
+    if (A.compact) {
+        // Compacted grid: every wave reads the batch's lengths and this
+        // workgroup takes the slot-th unit with pages of its KV head, the
+        // highest split index first (in dispatch order), so the slots past
+        // the last unit, which exit at once, come at the end.  A sequence
+        // with no page still has one unit (it writes its zero rows).
+        constexpr int kC = kCompactMaxBatch / 64;
+        int ns[kC], ln[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            const int s = c * 64 + lane;
+            ln[c] = s < (int)gridDim.y ? A.seq_lens[s] : 0;
+        }
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            const int np = (max(0, min(ln[c], A.max_pages * kPage)) + kPage - 1) / kPage;
+            ns[c] = c * 64 + lane < (int)gridDim.y ? max(1, splits_of(A, np)) : 0;
+        }
+        int slot = (int)(blockIdx.z * gridDim.y + blockIdx.y);
+        seq = -1;
+        for (int j = A.nsplit - 1; j >= 0 && seq < 0; --j) {
+#pragma unroll
+            for (int c = 0; c < kC; ++c) {
+                const uint64_t m = __builtin_amdgcn_ballot_w64(ns[c] > j);
+                const int n = __popcll(m);
+                if (seq < 0 && slot < n) {
+                    // the slot-th set bit of m
+                    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    const uint64_t hit = __builtin_amdgcn_ballot_w64(((m >> lane) & 1) && below == slot);
+                    const int l = __builtin_ffsll((long long)hit) - 1;
+                    seq = c * 64 + l;
+                    split = j;
+                    len_known = __builtin_amdgcn_readlane(ln[c], l);
+                }
+                if (seq < 0) slot -= n;
+            }
+        }
+        if (seq < 0) return;   // a slot past the last unit
+    }
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    split = __builtin_amdgcn_readfirstlane(split);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps per-wave values scalar
     const int q4 = lane >> 4, n16 = lane & 15;
     const int64_t head0 = (int64_t)seq * A.hq + (int64_t)kvh * G;
@@ -769,9 +830,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         wofs = first ? wave * fpw : kHalf * fpw + (wave - kHalf) * per;
         wcnt = first ? fpw : max(0, min(per, rest - (wave - kHalf) * per));
     };
-    const int p0 = split * A.pps;
+    const int p0 = split_start(A, split);
+    const int psz = split_start(A, split + 1) - p0;
     int wofs, wcnt;
-    wave_run(A.pps, wofs, wcnt);
+    wave_run(psz, wofs, wcnt);
     int ph_raw = bt_raw(p0 + wofs);
     int ph1_raw = TB != 0 ? bt_raw(p0 + wofs + 64) : 0;
     static_assert(kBufs >= 2, "at least one page in flight");
@@ -800,7 +862,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         st_k = A.app_k[((int64_t)seq * A.hkv + kvh) * D + min(tid, D - 1)];
         st_t = A.tau2[255 * kvh + min(tid, 254)];
     }
-    int len = A.seq_lens[seq];
+    int len = A.compact ? len_known : A.seq_lens[seq];
     __builtin_amdgcn_sched_barrier(0);   // (every load above is issued before the wait for len)
 
     const int len_in = len;   // (append: a length past the row is an error, not clamped)
@@ -831,8 +893,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             for (int e = threadIdx.x; e < G * D; e += kThreads) A.out[head0 * D + e] = 0.f;
         return;
     }
-    const int p1 = min(p0 + A.pps, npages);
-    if (p1 - p0 != A.pps) {   // the last split of its sequence: the wave's run moves
+    const int p1 = min(p0 + psz, npages);
+    if (p1 - p0 != psz) {   // the last split of its sequence: the wave's run moves
         wave_run(p1 - p0, wofs, wcnt);
         ph_raw = bt_raw(p0 + wofs);
         if constexpr (TB != 0) ph1_raw = bt_raw(p0 + wofs + 64);
@@ -1309,7 +1371,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // the counter for the next call.  No cache write-back or invalidation is
     // needed, since no plain store or load takes part. ----
     __shared__ int s_last;
-    const int ns_g = (npages + A.pps - 1) / A.pps;   // workgroups that work on this group
+    const int ns_g = splits_of(A, npages);   // workgroups that work on this group
     const int group = seq * A.hkv + kvh;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();

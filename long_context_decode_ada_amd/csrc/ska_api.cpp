@@ -385,28 +385,48 @@ ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, in
     if ((int64_t)batch * num_q_heads > (1ll << 30)) return SKA_ERR_UNSUPPORTED;
     if (scale == 0.f) scale = 1.0f / std::sqrt((float)d);
 
-    // split policy: pages per split (a multiple of the waves).  Automatic:
-    // as if every sequence had max_pages pages, one workgroup per CU.  When
-    // the (sequence, KV head) groups alone already fill the CUs that gives
-    // one split, and in a ragged batch the longest sequences then run alone
-    // at the end; so there every sequence is cut into up to kTailSplits
-    // splits (of at least kMinSplitPages pages), which the dispatcher hands
-    // to CUs as they free up.
-    constexpr int kTailSplits = 4, kMinSplitPages = 64;
-    int pps;
+    // Split policy.  Explicit: num_splits splits of equal size.  Automatic:
+    // as if every sequence had max_pages pages, with one workgroup per CU
+    // (equal splits).  When the (sequence, KV head) groups alone already
+    // fill the CUs, the batch runs in several rounds of workgroups, and the
+    // work units are sized so that the big ones go first and the small ones
+    // fill the last round: splits of kTailBase, kTailBase, 2 kTailBase, ...
+    // pages, doubling up to at most kTailBase << kTailMaxDoublings pages
+    // (and max_pages), handed out largest first; with a batch of at most
+    // kCompactMaxBatch the grid is also compacted (each workgroup finds its
+    // unit from the lengths, so no slot is spent on a split past the end of
+    // a short sequence).  Measured on a ragged batch of 64 (70..3546 pages)
+    // against four equal splits: 442 -> 387 us; a uniform batch of 64 x 2048
+    // pages within 1 %.
+    constexpr int kTailBase = 256, kTailMaxDoublings = 3;
+    int pps, split_m = 0;
+    bool rounds = false;
     if (num_splits > 0) {
         pps = (max_pages + num_splits - 1) / num_splits;
     } else {
         const int64_t total = (int64_t)batch * hkv * max_pages;
         const int64_t target = (int64_t)c->num_cus * decode_workgroups_per_cu();   // one round of resident workgroups
         pps = (int)std::min<int64_t>((total + target - 1) / target, max_pages);
-        if (pps >= max_pages) pps = std::max(kMinSplitPages, (max_pages + kTailSplits - 1) / kTailSplits);
+        if (pps >= max_pages) {
+            rounds = true;
+            pps = std::min(kTailBase, max_pages);
+            split_m = kTailMaxDoublings;
+        }
     }
     pps = ((pps + kWaves - 1) / kWaves) * kWaves;
     if (pps < kWaves) pps = kWaves;
+    while (split_m > 0 && ((int64_t)pps << split_m) > max_pages) --split_m;
     // the split index is the grid's z dimension (at most 65535)
-    if ((max_pages + pps - 1) / pps > 65535) pps = (((max_pages + 65534) / 65535 + kWaves - 1) / kWaves) * kWaves;
-    const int nsplit = (max_pages + pps - 1) / pps;
+    if (split_m == 0 && (max_pages + pps - 1) / pps > 65535)
+        pps = (((max_pages + 65534) / 65535 + kWaves - 1) / kWaves) * kWaves;
+    const int nsplit = [&] {   // splits of a sequence of max_pages pages (the kernel's layout)
+        const int cap = pps << split_m;
+        if (max_pages > cap) return split_m + (max_pages + cap - 1) / cap;
+        int k = 1;
+        while (k <= split_m + 1 && (pps << (k - 1)) < max_pages) ++k;
+        return k;
+    }();
+    if (nsplit > 65535) return SKA_ERR_UNSUPPORTED;
     if (batch > 65535 || hkv > 65535) return SKA_ERR_UNSUPPORTED;
 
     // workspace: [partial o | partial (m, l)]
@@ -451,6 +471,8 @@ ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, in
     da.hq = num_q_heads;
     da.max_pages = max_pages;
     da.pps = pps;
+    da.split_m = split_m;
+    da.compact = (rounds && batch <= kCompactMaxBatch) ? 1 : 0;
     da.nsplit = nsplit;
     da.tier_mask = c->pool.tier_mask;
     da.nt = c->nt;

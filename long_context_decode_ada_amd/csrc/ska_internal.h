@@ -79,6 +79,9 @@ struct EncodeArgs {
 };
 
 
+// largest batch whose lengths every decode workgroup reads to find its unit
+constexpr int kCompactMaxBatch = 512;
+
 struct DecodeArgs {
     const uint8_t *kcode;
     const uint64_t *page_off;
@@ -103,8 +106,12 @@ struct DecodeArgs {
     int64_t num_pages;
     int64_t page_stride;
     int hkv, hq, max_pages;
-    int pps;                 // pages per split (multiple of kWaves)
+    int pps;                 // pages of the smallest split (multiple of kWaves)
+    int split_m;             // split sizes: pps, pps, 2 pps, ..., pps << split_m, then
+                             // pps << split_m each (0: every split has pps pages)
     int nsplit;
+    int compact;             // 1: workgroup slots map to the (sequence, split) units
+                             // with pages, largest splits first (batch <= kCompactMaxBatch)
     uint32_t tier_mask;
     int nt;
     int8_t tslot[9];         // tier b -> index among the tiers present

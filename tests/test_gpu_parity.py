@@ -177,3 +177,29 @@ def test_more_splits_than_one_merge_round():
     compare(w, g64, o, rng, label="64 splits")
     g0 = gpu_run(w)
     assert np.abs(g64["out"] - g0["out"]).max() < 1e-4
+
+
+def test_multi_round_batch_split_layout():
+    """A batch whose (sequence, KV head) groups alone fill the CUs runs in
+    rounds of workgroups: by default its splits double in size from 256
+    pages and the grid is compacted (each workgroup finds its unit from the
+    lengths).  Ragged lengths up to 1024 pages, with an empty row, a
+    one-token row and rows on and next to the split boundaries (256, 512
+    pages), match the oracle, and equal splits give the same output."""
+    w = W.make("ragged_b64", 1 / 4, batch=40)                 # 40 x 8 groups, up to 16384 tokens
+    lens = w.seq_lens.copy()
+    order = np.argsort(-lens, kind="stable")                   # longest first
+    for i, n in zip(order[1:5], [512 * 16 + 16, 512 * 16 - 1, 256 * 16 + 1, 256 * 16]):
+        assert lens[i] >= n
+        lens[i] = n
+    lens[order[-1]], lens[order[-2]] = 0, 1
+    say("[rounds] B=%d max_pages=%d lengths %s" % (w.B, w.max_pages, lens.tolist()))
+    assert lens.max() > 512 * 16
+    rng = O.calibrate(w.keys)
+    g = gpu_run(w, seq_lens=lens)
+    o = oracle_run(w, rng, seq_lens=lens)
+    assert not g["out"][order[-1]].any()
+    assert g["errors"] == 0
+    compare(w, g, o, rng, seq_lens=lens, label="rounds")
+    g4 = gpu_run(w, seq_lens=lens, num_splits=4, want_logits=False)
+    assert np.abs(g4["out"] - g["out"]).max() < 1e-4
