@@ -1000,8 +1000,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // only covers the loads of the page being computed.
     PageBuf<D> R[kBufs];
     PageDesc dd[kBufs];
-    auto start_chunk = [&](int c0, int ph) {
-        page_list(c0, ph);
+    auto issue_chunk = [&]() {
         // issued even when the chunk has no valid page (then through empty
         // descriptors that read nothing), so every path issues the same loads
 #pragma unroll
@@ -1011,8 +1010,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             load_page<D, TB>(A, dd[i], kvh, R[i]);
         }
     };
-    // (pools of mixed tiers start after the preparation: their larger
-    // kernel has no registers to spare for two pages during it)
+    auto start_chunk = [&](int c0, int ph) {
+        page_list(c0, ph);
+        issue_chunk();
+    };
+    // (pools of mixed tiers build the first chunk's page list before the
+    // query preparation and issue its page loads after it: two page buffers
+    // held across the preparation would spill)
     // Single tier: the wave walks its pages in order, reading the block
     // table 64 entries (one per lane) at a time into two rotating register
     // slots, the next slot always requested a chunk ahead; the page loads
@@ -1067,6 +1071,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                 }
             }
         }
+    }
+
+    // mixed tiers: the first chunk's headers and offsets are read now, so
+    // their round trip runs under the query preparation
+    if constexpr (TB == 0) {
+        if (wp0 < wp1) page_list(wp0, ph_first);
     }
 
     // Query prep, section 2.1's c_q: per tier, the angle codes of each query
@@ -1303,7 +1313,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     int ph_next = -1;   // the next chunk's block-table entries, requested a chunk ahead
     for (int c0 = wp0; TB == 0 && c0 < wp1; c0 += 64) {
         if (c0 != wp0) start_chunk(c0, ph_next);
-        else if (TB == 0) start_chunk(c0, ph_first);
+        else issue_chunk();   // (its page list was built before the query preparation)
         ph_next = bt_raw(c0 + 64);
         ph_next = (c0 + 64 + lane < wp1) ? ph_next : -1;   // (all -1 past the wave's run)
         if (nvalid == 0) continue;
