@@ -132,7 +132,13 @@ ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool,
  *   block_table  device int32 [batch][max_pages]
  *   seq_lens     device int32 [batch] (0 gives a zero output row)
  *   scale        softmax scale; 0 means 1/sqrt(d)
- *   num_splits   page splits per sequence (split-T); 0 chooses
+ *   num_splits   page splits per sequence (split-T).  > 0: that many
+ *                equal splits of max_pages pages.  0 (automatic): equal
+ *                splits sized for one workgroup per CU when the (sequence,
+ *                KV head) groups do not fill the CUs on their own; else
+ *                splits doubling from 256 pages (256, 256, 512, 1024, then
+ *                2048 each, capped at max_pages), the largest handed out
+ *                first.  Results agree across split counts to rounding.
  *   out          device fp32 [batch][num_q_heads][d]
  *   logits_dbg   device fp32 [batch][num_q_heads][max_pages*16] or NULL;
  *                receives l_t (natural units) at each resident position

@@ -149,7 +149,7 @@ hipError_t upload(T **dst, const T *src, size_t count) {
 }
 
 void prof_clear(ska_cache *c) {
-    for (hipEvent_t e : c->prof_ev) hipEventDestroy(e);
+    for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
     c->prof_ev.clear();
     c->prof_max = c->prof_n = 0;
 }
@@ -157,15 +157,15 @@ void prof_clear(ska_cache *c) {
 void release(ska_cache *c) {
     if (!c) return;
     prof_clear(c);
-    hipFree(c->d_cos2);
-    hipFree(c->d_sin2);
-    hipFree(c->d_cen);
-    hipFree(c->d_tau2);
-    hipFree(c->d_lut);
-    hipFree(c->d_rlev);
-    hipFree(c->d_err);
-    hipFree(c->d_ws);
-    hipFree(c->d_cnt);
+    (void)hipFree(c->d_cos2);
+    (void)hipFree(c->d_sin2);
+    (void)hipFree(c->d_cen);
+    (void)hipFree(c->d_tau2);
+    (void)hipFree(c->d_lut);
+    (void)hipFree(c->d_rlev);
+    (void)hipFree(c->d_err);
+    (void)hipFree(c->d_ws);
+    (void)hipFree(c->d_cnt);
     delete c;
 }
 
@@ -209,8 +209,8 @@ ska_status set_range(ska_cache *c, const double *range) {
     std::vector<double> tau2(255 * (size_t)hkv);
     for (int g = 0; g < hkv; ++g)
         build_radius(c->pool.radius_mode, range[2 * g], range[2 * g + 1], lev.data() + 256 * g, tau2.data() + 255 * g);
-    hipFree(c->d_rlev);
-    hipFree(c->d_tau2);
+    (void)hipFree(c->d_rlev);
+    (void)hipFree(c->d_tau2);
     c->d_rlev = nullptr;
     c->d_tau2 = nullptr;
     hipError_t e = upload(&c->d_rlev, lev.data(), lev.size());
@@ -231,7 +231,7 @@ ska_status calibrate(ska_cache *c, const float *keys, int64_t n, hipStream_t s) 
     if (e == hipSuccess) e = launch_calibrate(keys, n, hkv, c->pool.d, d_mm, s);
     if (e == hipSuccess) e = hipMemcpyAsync(mm.data(), d_mm, mm.size() * sizeof(mm[0]), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    hipFree(d_mm);
+    (void)hipFree(d_mm);
     if (e != hipSuccess) return SKA_ERR_HIP;
     std::vector<double> range(2 * (size_t)hkv);
     for (int g = 0; g < hkv; ++g) {
