@@ -203,3 +203,19 @@ def test_multi_round_batch_split_layout():
     compare(w, g, o, rng, seq_lens=lens, label="rounds")
     g4 = gpu_run(w, seq_lens=lens, num_splits=4, want_logits=False)
     assert np.abs(g4["out"] - g["out"]).max() < 1e-4
+
+
+@pytest.mark.parametrize("scale,batch", [(1 / 8, 130), (1 / 512, 600)])
+def test_multi_round_batches_past_one_wave_of_lengths(scale, batch):
+    """Multi-round batches whose lengths the compacted grid reads in several
+    64-sequence chunks (130 sequences, the last chunk partly filled, two
+    split levels), and one past the compaction limit of 512 sequences (600
+    short sequences: doubling layout without compaction).  Both match the
+    oracle."""
+    w = W.make("ragged_b64", scale, batch=batch)
+    say("[rounds] B=%d max_pages=%d tokens=%d" % (w.B, w.max_pages, w.n_tokens))
+    rng = O.calibrate(w.keys)
+    g = gpu_run(w)
+    o = oracle_run(w, rng)
+    assert g["errors"] == 0
+    compare(w, g, o, rng, label="rounds B=%d" % batch)
