@@ -21,6 +21,7 @@ CASES = [
     ("gqa_t32k", 1 / 32, None),
     ("ragged_b64", 1 / 32, None),
     ("mixed_tiers", 1 / 16, 4),
+    ("ragged_b64", 1 / 4, 40),    # several rounds: doubling splits, compacted grid
 ]
 
 
