@@ -246,7 +246,6 @@ __global__ __launch_bounds__(kRdrThreads) void k_rdr_round(RdrArgs A, int r) {
             if (f > 1.0) f = 1.0;
             dk[k] = ud * f;
         }
-#pragma unroll
         for (int m = 0; m < 15; ++m) {
             if (m >= nl) break;
             long long bb = 0;
