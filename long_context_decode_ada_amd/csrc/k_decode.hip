@@ -1391,12 +1391,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     __syncthreads();
     if (!s_last) return;
+    auto ld = [](float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    constexpr int kMergeMax = 256;   // splits whose weights one LDS pass holds
+    if (ns_g <= kMergeMax) {
+        // Each split's weight, once per head (one wave per head, in the LDS
+        // of the in-workgroup merge, which is done): w_s = 2^(m_s - M) with M
+        // the largest partial max, and L = sum_s w_s l_s.  Each output
+        // element then needs only its own partials: O = sum_s w_s o_s.
+        static_assert(G * kMergeMax + G <= kWaves * 2 * G * D, "merge weights fit the merge LDS");
+        float *W = &mo[0][0][0];          // [G][kMergeMax]
+        float *Lh = W + G * kMergeMax;    // [G]; 0 for a group without tokens
+        if (wave < G) {
+            float *ml = A.part_ml + (head0 + wave) * A.nsplit * 2;
+            constexpr int kPer = kMergeMax / 64;
+            float pm[kPer], pl[kPer];
+            float M = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int sp = lane + 64 * i;
+                pm[i] = sp < ns_g ? ld(ml + 2 * sp) : -INFINITY;
+                pl[i] = sp < ns_g ? ld(ml + 2 * sp + 1) : 0.f;
+                M = fmaxf(M, pm[i]);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+            float L = 0.f;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const float w = (pm[i] != -INFINITY) ? exp2f(pm[i] - M) : 0.f;
+                W[wave * kMergeMax + lane + 64 * i] = w;
+                L += w * pl[i];
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+            if (lane == 0) Lh[wave] = (M != -INFINITY) ? L : 0.f;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < G * D; idx += kThreads) {
+            const int h = idx / D, e = idx % D;
+            const int64_t row = head0 + h;
+            float *po = A.part_o + row * A.nsplit * D + e;
+            constexpr int kMB = 16;   // partials requested at once
+            float O = 0.f;
+            for (int sp0 = 0; sp0 < ns_g; sp0 += kMB) {
+                float pv[kMB];
+#pragma unroll
+                for (int i = 0; i < kMB; ++i) pv[i] = sp0 + i < ns_g ? ld(po + (int64_t)(sp0 + i) * D) : 0.f;
+#pragma unroll
+                for (int i = 0; i < kMB; ++i)
+                    if (sp0 + i < ns_g) O += W[h * kMergeMax + sp0 + i] * pv[i];
+            }
+            const float L = Lh[h];
+            A.out[row * D + e] = L > 0.f ? O / L : 0.f;
+        }
+        if (tid == 0) __hip_atomic_store(&A.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     for (int idx = tid; idx < G * D; idx += kThreads) {
         const int h = idx / D, e = idx % D;
         const int64_t row = head0 + h;
         float *ml = A.part_ml + row * A.nsplit * 2;
         float *po = A.part_o + row * A.nsplit * D + e;
-        auto ld = [](float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
         // up to kMB splits' partials are requested at once, then folded into
         // the running (M, L, O) in split order
         constexpr int kMB = 16;
