@@ -38,11 +38,21 @@
  * Memory: every pointer argument marked "device" is caller-owned device
  * memory (any allocator; PyTorch in the tests).  The library owns only what
  * it allocates inside a ska_cache (code tables, radius tables, the decode
- * workspace) and frees it in ska_free.
+ * workspace) and frees it in ska_free.  Everything a cache owns is
+ * allocated when it is created (the first ska_encode_keys), the decode
+ * workspace sized from the maxima the pool descriptor declares; no later
+ * call on a cache allocates or frees device memory.
  *
  * Streams: `stream` is a hipStream_t (NULL = the null stream).  All work is
- * enqueued asynchronously on it.  The only host synchronisation is the
- * calibrating ska_encode_keys call (it reads the radius range back).
+ * enqueued asynchronously on it.  Host synchronisation happens only in the
+ * calibrating ska_encode_keys call (it reads the radius range back),
+ * ska_device_errors, ska_profile_read, and ska_rdr_plan when its workspace
+ * grows (see there).  The decode calls of one cache share its workspace and
+ * merge counters, so they run one after another on the device: a decode call
+ * on a different stream than the cache's previous decode call is ordered
+ * after that call (an event recorded on the previous stream, waited on by
+ * the new one; the previous stream must still exist).  Calls on one cache
+ * from several host threads at once are not supported.
  *
  * Errors: arguments are checked on the host before any HIP call; a bad one
  * returns SKA_ERR_INVALID (or SKA_ERR_UNSUPPORTED for a legal but unbuilt
@@ -70,6 +80,7 @@ typedef enum {
 
 enum { SKA_RADIUS_UNIFORM = 0, SKA_RADIUS_LOG = 1 };
 enum { SKA_Q_CODED = 0, SKA_Q_EXACT = 1 };
+enum { SKA_QDIR_F16 = 0, SKA_QDIR_F32 = 1 };
 enum { SKA_PAGE_SIZE = 16 };
 
 /* Device error flags (ska_device_errors). */
@@ -102,13 +113,29 @@ typedef struct {
                                  token, head and layer): page_bits [num_pages][Hkv] holds
                                  the header of each KV head's 16 records and page_off
                                  (required) [num_pages][Hkv] their byte offset */
+    int query_precision;      /* precision of the query direction inside f_b (section 2.1's
+                                 logit |q| r~ f_b): SKA_QDIR_F16 (default) rounds it to binary16,
+                                 which moves a logit by at most 2^-11 (typically ~1e-4 at
+                                 d = 128) of its bound scale*|q|*r~; SKA_QDIR_F32 keeps binary32
+                                 (for keys with outlier channels, whose large radii turn that
+                                 into large output errors; about 20 % slower) */
+    /* Maxima of the decode calls on this cache, fixed when it is created:
+       they size the decode workspace (split partials and merge counters),
+       which is allocated then and never again.  A decode call outside them
+       returns SKA_ERR_INVALID. */
+    int max_batch;            /* >= 1: sequences per call */
+    int max_heads_q;          /* >= 1: query heads per call */
+    int max_pages;            /* >= 1: block-table row length */
+    int max_splits;           /* >= 0: largest explicit num_splits (0: automatic only) */
 } ska_pool_desc;
 
 /* ska_encode_keys -- the write path of section 2.3: map dense keys to
  * spherical codes (section 2.1) and store them, with their values, in the
  * paged pools.
- *   cache   in/out.  *cache == NULL creates a cache for `pool`; otherwise the
- *           pool must have the same shape fields as at creation.
+ *   cache   in/out.  *cache == NULL creates a cache for `pool` (tables and
+ *           the decode workspace for the pool's declared maxima); otherwise
+ *           the pool must have the same shape, precision and maxima fields
+ *           as at creation.
  *   keys    device fp32 [n][Hkv][d]
  *   values  device bf16 [n][Hkv][d] or NULL (values not written)
  *   slot    device int64 [n]: phys*16 + token-in-page for each key
@@ -142,8 +169,11 @@ ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool,
  *   out          device fp32 [batch][num_q_heads][d]
  *   logits_dbg   device fp32 [batch][num_q_heads][max_pages*16] or NULL;
  *                receives l_t (natural units) at each resident position
- * Hq/Hkv must be 1, 2 or 4.  Returns SKA_OK. */
-ska_status ska_decode_attention(ska_cache *cache, const float *q, int batch, int num_q_heads,
+ *                (the same kernel as without it, plus the logit stores)
+ * Hq/Hkv must be 1, 2 or 4.  batch, num_q_heads, max_pages and an explicit
+ * num_splits must lie within the cache's declared maxima (else
+ * SKA_ERR_INVALID, nothing enqueued).  Allocates nothing.  Returns SKA_OK. */
+ska_status ska_decode_attention(const ska_cache *cache, const float *q, int batch, int num_q_heads,
                                 const int32_t *block_table, int max_pages,
                                 const int32_t *seq_lens, float scale, int num_splits,
                                 float *out, float *logits_dbg, void *stream);
@@ -170,7 +200,7 @@ ska_status ska_decode_attention(ska_cache *cache, const float *q, int batch, int
  * outside tier_mask sets SKA_DEVERR_TIER.  Argument errors are those of
  * ska_decode_attention, plus SKA_ERR_INVALID for NULL new_keys/new_values
  * with batch > 0; a rejected call stores nothing.  Returns SKA_OK. */
-ska_status ska_append_decode_attention(ska_cache *cache, const float *new_keys, const uint16_t *new_values,
+ska_status ska_append_decode_attention(const ska_cache *cache, const float *new_keys, const uint16_t *new_values,
                                        const float *q, int batch, int num_q_heads,
                                        const int32_t *block_table, int max_pages,
                                        const int32_t *seq_lens, float scale, int num_splits,
@@ -187,7 +217,7 @@ ska_status ska_append_decode_attention(ska_cache *cache, const float *new_keys, 
  *            caller or by ska_decompress_keys; read, never written
  *   other arguments as ska_decode_attention.
  * Returns SKA_ERR_INVALID for a NULL k_dense; errors as ska_decode_attention. */
-ska_status ska_dense_decode_attention(ska_cache *cache, const uint16_t *k_dense, const float *q, int batch,
+ska_status ska_dense_decode_attention(const ska_cache *cache, const uint16_t *k_dense, const float *q, int batch,
                                       int num_q_heads, const int32_t *block_table, int max_pages,
                                       const int32_t *seq_lens, float scale, int num_splits, float *out,
                                       float *logits_dbg, void *stream);
@@ -200,7 +230,7 @@ ska_status ska_dense_decode_attention(ska_cache *cache, const uint16_t *k_dense,
  * ska_dense_decode_attention; other pages are left untouched).  Pages whose
  * id or header is out of range are skipped and flagged (ska_device_errors).
  * batch is at most 65535 and max_pages at most 64 * 65535.  Returns SKA_OK. */
-ska_status ska_decompress_keys(ska_cache *cache, const int32_t *block_table, int batch, int max_pages,
+ska_status ska_decompress_keys(const ska_cache *cache, const int32_t *block_table, int batch, int max_pages,
                                const int32_t *seq_lens, uint16_t *k_dense, void *stream);
 
 /* Rate-distortion retention parameters (section 2.2 of the page): the tier

@@ -2,7 +2,8 @@
 
     python -m long_context_decode_ada_amd.build [--jobs N]
 
-Compiles the kernel translation units and the host API with hipcc and links
+Compiles the kernel translation units (the decode kernels once per head
+dimension and group size) and the host API with hipcc and links
 them into long_context_decode_ada_amd/libska.so.  The encode/query-code unit
 and the host API are built with -ffp-contract=off (their binary64 decisions
 must be rounded exactly as written); the decode unit may contract.
@@ -26,16 +27,20 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I" + os.path
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
 
-UNITS = {
-    "k_decode.hip": [],
-    "k_codes.hip": ["-ffp-contract=off"],
-    "k_rdr.hip": ["-ffp-contract=off"],
-    "ska_api.cpp": ["-ffp-contract=off", "-fno-builtin"],
-}
+# (object name, source, extra flags).  The decode kernel families (head
+# dimension x group size x query precision) are one source built once per
+# family, so that they compile in parallel.
+UNITS = [(f"k_decode_{d}_{g}_{q}", "k_decode_inst.hip", [f"-DSKA_INST_D={d}", f"-DSKA_INST_G={g}", f"-DSKA_INST_QF={q}"])
+         for d in (128, 64) for g in (4, 2, 1) for q in (0, 1)] + [
+    ("k_decode", "k_decode.hip", []),
+    ("k_codes", "k_codes.hip", ["-ffp-contract=off"]),
+    ("k_rdr", "k_rdr.hip", ["-ffp-contract=off"]),
+    ("ska_api", "ska_api.cpp", ["-ffp-contract=off", "-fno-builtin"]),
+]
 
 
-def _compile(src: str, extra: list) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(name: str, src: str, extra: list) -> str:
+    obj = os.path.join(BUILD, name + ".o")
     lang = ["-x", "hip"]
     cmd = ["hipcc", *lang, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,10 +49,12 @@ def _compile(src: str, extra: list) -> str:
     return obj
 
 
-def build(jobs: int = 3, verbose: bool = False) -> str:
+def build(jobs: int = 0, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    if jobs <= 0:
+        jobs = min(len(UNITS), os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), UNITS.items()))
+        objs = list(ex.map(lambda u: _compile(*u), UNITS))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,6 +68,6 @@ def build(jobs: int = 3, verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
-    ap.add_argument("--jobs", type=int, default=3)
+    ap.add_argument("--jobs", type=int, default=0, help="parallel compiles (0: one per CPU, at most one per unit)")
     args = ap.parse_args()
     build(args.jobs, verbose=True)

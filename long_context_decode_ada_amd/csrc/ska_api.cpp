@@ -39,13 +39,21 @@ struct ska_cache {
     float2 *d_lut = nullptr;
     float *d_rlev = nullptr;
     uint32_t *d_err = nullptr;
+    // decode workspace, allocated at creation for the pool's declared maxima:
+    // split partials (ws_rows rows of (o[d], m, l)) and the per-(sequence,
+    // KV head) counters of the in-kernel merge (zero between calls)
     void *d_ws = nullptr;
-    size_t ws_bytes = 0;
-    uint32_t *d_cnt = nullptr;   // per (sequence, KV head) counters of the in-kernel merge
+    size_t ws_rows = 0;
+    uint32_t *d_cnt = nullptr;
     size_t cnt_n = 0;
+    // stream of the last decode call (calls share the workspace) and the
+    // event that orders a call on another stream after it
+    mutable hipStream_t last_stream = nullptr;
+    hipEvent_t order_ev = nullptr;
     // kernel timing (ska_profile_begin / ska_profile_read)
     std::vector<hipEvent_t> prof_ev;  // 2 per recorded call
-    int prof_max = 0, prof_n = 0;
+    int prof_max = 0;
+    mutable int prof_n = 0;
 };
 
 namespace {
@@ -70,13 +78,89 @@ ska_status check_pool(const ska_pool_desc *p) {
     if (!p->kcode || !p->rcode || !p->v || !p->page_bits) return SKA_ERR_INVALID;
     if (p->head_tiers != 0 && p->head_tiers != 1) return SKA_ERR_INVALID;
     if (p->head_tiers && !p->page_off) return SKA_ERR_INVALID;
+    if (p->query_precision != SKA_QDIR_F16 && p->query_precision != SKA_QDIR_F32) return SKA_ERR_INVALID;
+    if (p->max_batch < 1 || p->max_heads_q < 1 || p->max_pages < 1 || p->max_splits < 0) return SKA_ERR_INVALID;
+    if (p->max_heads_q % p->num_kv_heads != 0) return SKA_ERR_INVALID;
     return SKA_OK;
 }
 
 bool same_shape(const ska_pool_desc &a, const ska_pool_desc &b) {
     return a.d == b.d && a.num_kv_heads == b.num_kv_heads && a.page_size == b.page_size &&
            a.num_pages == b.num_pages && a.radius_mode == b.radius_mode && a.radius_bits == b.radius_bits &&
-           a.tier_mask == b.tier_mask && a.query_mode == b.query_mode && a.head_tiers == b.head_tiers;
+           a.tier_mask == b.tier_mask && a.query_mode == b.query_mode && a.head_tiers == b.head_tiers &&
+           a.query_precision == b.query_precision && a.max_batch == b.max_batch &&
+           a.max_heads_q == b.max_heads_q && a.max_pages == b.max_pages && a.max_splits == b.max_splits;
+}
+
+// Split layout of a decode call (the kernel's split_start/splits_of read it).
+// Explicit: num_splits splits of equal size.  Automatic: as if every
+// sequence had max_pages pages, with one workgroup per CU (equal splits).
+// When the (sequence, KV head) groups alone already fill the CUs, the batch
+// runs in several rounds of workgroups, and the work units are sized so that
+// the big ones go first and the small ones fill the last round: splits of
+// kTailBase, kTailBase, 2 kTailBase, ... pages, doubling up to at most
+// kTailBase << kTailMaxDoublings pages (and max_pages), handed out largest
+// first; with a batch of at most kCompactMaxBatch the grid is also compacted
+// (each workgroup finds its unit from the lengths, so no slot is spent on a
+// split past the end of a short sequence).  Measured on a ragged batch of 64
+// (70..3546 pages) against four equal splits: 442 -> 387 us; a uniform batch
+// of 64 x 2048 pages within 1 %.
+constexpr int kTailBase = 256, kTailMaxDoublings = 3;
+struct SplitLayout {
+    int pps = 0, split_m = 0, nsplit = 0;
+    bool rounds = false;
+};
+SplitLayout split_layout(int num_cus, int batch, int hkv, int max_pages, int num_splits) {
+    SplitLayout L;
+    int pps;
+    if (num_splits > 0) {
+        pps = (max_pages + num_splits - 1) / num_splits;
+    } else {
+        const int64_t total = (int64_t)batch * hkv * max_pages;
+        const int64_t target = (int64_t)num_cus * decode_workgroups_per_cu();   // one round of resident workgroups
+        pps = (int)std::min<int64_t>((total + target - 1) / target, max_pages);
+        if (pps >= max_pages) {
+            L.rounds = true;
+            pps = std::min(kTailBase, max_pages);
+            L.split_m = kTailMaxDoublings;
+        }
+    }
+    pps = ((pps + kWaves - 1) / kWaves) * kWaves;
+    if (pps < kWaves) pps = kWaves;
+    while (L.split_m > 0 && ((int64_t)pps << L.split_m) > max_pages) --L.split_m;
+    // the split index is the grid's z dimension (at most 65535)
+    if (L.split_m == 0 && (max_pages + pps - 1) / pps > 65535)
+        pps = (((max_pages + 65534) / 65535 + kWaves - 1) / kWaves) * kWaves;
+    L.pps = pps;
+    const int cap = pps << L.split_m;   // splits of a sequence of max_pages pages (the kernel's layout)
+    if (max_pages > cap) {
+        L.nsplit = L.split_m + (max_pages + cap - 1) / cap;
+    } else {
+        int k = 1;
+        while (k <= L.split_m + 1 && (pps << (k - 1)) < max_pages) ++k;
+        L.nsplit = k;
+    }
+    return L;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// workspace of `rows` partial rows: [o: rows x d floats | (m, l): rows x 2 floats]
+inline size_t ws_off_ml(size_t rows, int d) { return align256(rows * (size_t)d * 4); }
+inline size_t ws_bytes(size_t rows, int d) { return ws_off_ml(rows, d) + align256(rows * 2 * 4); }
+
+// Partial rows (sequence, query head, split) that any decode call within the
+// pool's maxima can need.  Per query head, a call's batch * nsplit is at most:
+// automatic layout, one round: batch * ceil(target / (batch * Hkv)) <=
+// target / Hkv + batch (each split is at least total / target pages);
+// several rounds: batch * ceil(max_pages / kTailBase) (each split but a
+// sequence's last is at least kTailBase pages); explicit: batch * num_splits.
+size_t reserve_rows(const ska_pool_desc &p, int num_cus) {
+    const int64_t target = (int64_t)num_cus * decode_workgroups_per_cu();
+    const int64_t B = p.max_batch, hkv = p.num_kv_heads;
+    int64_t per_head = std::max<int64_t>((target + hkv - 1) / hkv + B,
+                                         B * std::max<int64_t>(1, (p.max_pages + kTailBase - 1) / kTailBase));
+    per_head = std::max<int64_t>(per_head, B * (int64_t)p.max_splits);
+    return (size_t)per_head * (size_t)p.max_heads_q;
 }
 
 // cos^2, sin^2 of the bin edges j*pi/2^b for b = 1..8 at offset 2^b - 2.
@@ -166,6 +250,7 @@ void release(ska_cache *c) {
     (void)hipFree(c->d_err);
     (void)hipFree(c->d_ws);
     (void)hipFree(c->d_cnt);
+    if (c->order_ev) (void)hipEventDestroy(c->order_ev);
     delete c;
 }
 
@@ -194,6 +279,13 @@ ska_status create(ska_cache **out, const ska_pool_desc *pool) {
     if (e == hipSuccess) e = upload(&c->d_lut, lut.data(), lut.size());
     uint32_t zero = 0;
     if (e == hipSuccess) e = upload(&c->d_err, &zero, 1);
+    // the decode workspace for every call within the declared maxima
+    c->ws_rows = reserve_rows(*pool, c->num_cus);
+    if (e == hipSuccess) e = hipMalloc(&c->d_ws, ws_bytes(c->ws_rows, pool->d));
+    c->cnt_n = (size_t)pool->max_batch * pool->num_kv_heads;
+    if (e == hipSuccess) e = hipMalloc((void **)&c->d_cnt, c->cnt_n * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(c->d_cnt, 0, c->cnt_n * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->order_ev, hipEventDisableTiming);
     if (e != hipSuccess) {
         release(c);
         return e == hipErrorOutOfMemory ? SKA_ERR_NOMEM : SKA_ERR_HIP;
@@ -244,43 +336,6 @@ ska_status calibrate(ska_cache *c, const float *keys, int64_t n, hipStream_t s) 
     }
     return set_range(c, range.data());
 }
-
-// Counters of the in-kernel split merge: zero when allocated; each call
-// leaves them zero (the merging workgroup clears its group's counter).
-ska_status ensure_counters(ska_cache *c, size_t n, hipStream_t s) {
-    if (n <= c->cnt_n) return SKA_OK;
-    if (c->d_cnt) {
-        if (hipFree(c->d_cnt) != hipSuccess) return SKA_ERR_HIP;
-        c->d_cnt = nullptr;
-        c->cnt_n = 0;
-    }
-    const size_t want = n + n / 4 + 64;
-    if (hipMalloc(&c->d_cnt, want * sizeof(uint32_t)) != hipSuccess) {
-        c->d_cnt = nullptr;
-        return SKA_ERR_NOMEM;
-    }
-    if (launch_zero_u32(c->d_cnt, (int64_t)want, s) != hipSuccess) return SKA_ERR_HIP;
-    c->cnt_n = want;
-    return SKA_OK;
-}
-
-ska_status ensure_ws(ska_cache *c, size_t bytes, hipStream_t s) {
-    if (bytes <= c->ws_bytes) return SKA_OK;
-    if (c->d_ws) {
-        if (hipFree(c->d_ws) != hipSuccess) return SKA_ERR_HIP;  // hipFree waits for work using it
-        c->d_ws = nullptr;
-        c->ws_bytes = 0;
-    }
-    size_t want = bytes + bytes / 4;
-    if (hipMalloc(&c->d_ws, want) != hipSuccess) {
-        c->d_ws = nullptr;
-        return SKA_ERR_NOMEM;
-    }
-    c->ws_bytes = want;
-    return SKA_OK;
-}
-
-inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -367,82 +422,36 @@ ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool, const f
 
 namespace {
 
-// One decode call: ADA over the cache's coded pools (k_dense NULL) or, for
-// the dense baseline, over bf16 keys k_dense with the cache's values.
-ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, int batch, int num_q_heads,
-                       const int32_t *block_table, int max_pages, const int32_t *seq_lens,
-                       float scale, int num_splits, float *out, float *logits_dbg, void *stream,
-                       const float *app_k = nullptr, const uint16_t *app_v = nullptr) {
+// Checks of one decode call and its kernel arguments, the split workspace
+// left empty: ADA over the cache's coded pools (k_dense NULL) or, for the
+// dense baseline, over bf16 keys k_dense with the cache's values.  Returns
+// SKA_OK with *rows = the partial rows (sequence, query head, split) the call
+// uses, or an error (nothing to launch; *rows = 0 for an empty batch).
+ska_status prepare_decode(const ska_cache *c, const uint16_t *k_dense, const float *q, int batch,
+                          int num_q_heads, const int32_t *block_table, int max_pages, const int32_t *seq_lens,
+                          float scale, int num_splits, float *out, float *logits_dbg, const float *app_k,
+                          const uint16_t *app_v, DecodeArgs &da, int &G, size_t &rows) {
+    rows = 0;
     if (!c) return SKA_ERR_INVALID;
     if (batch < 0 || num_q_heads < 1 || max_pages < 1 || num_splits < 0) return SKA_ERR_INVALID;
     if (!std::isfinite(scale) || scale < 0.f) return SKA_ERR_INVALID;
     const int hkv = c->pool.num_kv_heads, d = c->pool.d;
     if (num_q_heads % hkv != 0) return SKA_ERR_INVALID;
-    const int G = num_q_heads / hkv;
+    G = num_q_heads / hkv;
     if (G != 1 && G != 2 && G != 4) return SKA_ERR_UNSUPPORTED;
+    // within the maxima the cache's workspace was sized for
+    if (batch > c->pool.max_batch || num_q_heads > c->pool.max_heads_q || max_pages > c->pool.max_pages ||
+        num_splits > c->pool.max_splits)
+        return SKA_ERR_INVALID;
     if (batch == 0) return SKA_OK;
     if (!q || !block_table || !seq_lens || !out) return SKA_ERR_INVALID;
-    if ((int64_t)batch * num_q_heads > (1ll << 30)) return SKA_ERR_UNSUPPORTED;
-    if (scale == 0.f) scale = 1.0f / std::sqrt((float)d);
-
-    // Split policy.  Explicit: num_splits splits of equal size.  Automatic:
-    // as if every sequence had max_pages pages, with one workgroup per CU
-    // (equal splits).  When the (sequence, KV head) groups alone already
-    // fill the CUs, the batch runs in several rounds of workgroups, and the
-    // work units are sized so that the big ones go first and the small ones
-    // fill the last round: splits of kTailBase, kTailBase, 2 kTailBase, ...
-    // pages, doubling up to at most kTailBase << kTailMaxDoublings pages
-    // (and max_pages), handed out largest first; with a batch of at most
-    // kCompactMaxBatch the grid is also compacted (each workgroup finds its
-    // unit from the lengths, so no slot is spent on a split past the end of
-    // a short sequence).  Measured on a ragged batch of 64 (70..3546 pages)
-    // against four equal splits: 442 -> 387 us; a uniform batch of 64 x 2048
-    // pages within 1 %.
-    constexpr int kTailBase = 256, kTailMaxDoublings = 3;
-    int pps, split_m = 0;
-    bool rounds = false;
-    if (num_splits > 0) {
-        pps = (max_pages + num_splits - 1) / num_splits;
-    } else {
-        const int64_t total = (int64_t)batch * hkv * max_pages;
-        const int64_t target = (int64_t)c->num_cus * decode_workgroups_per_cu();   // one round of resident workgroups
-        pps = (int)std::min<int64_t>((total + target - 1) / target, max_pages);
-        if (pps >= max_pages) {
-            rounds = true;
-            pps = std::min(kTailBase, max_pages);
-            split_m = kTailMaxDoublings;
-        }
-    }
-    pps = ((pps + kWaves - 1) / kWaves) * kWaves;
-    if (pps < kWaves) pps = kWaves;
-    while (split_m > 0 && ((int64_t)pps << split_m) > max_pages) --split_m;
-    // the split index is the grid's z dimension (at most 65535)
-    if (split_m == 0 && (max_pages + pps - 1) / pps > 65535)
-        pps = (((max_pages + 65534) / 65535 + kWaves - 1) / kWaves) * kWaves;
-    const int nsplit = [&] {   // splits of a sequence of max_pages pages (the kernel's layout)
-        const int cap = pps << split_m;
-        if (max_pages > cap) return split_m + (max_pages + cap - 1) / cap;
-        int k = 1;
-        while (k <= split_m + 1 && (pps << (k - 1)) < max_pages) ++k;
-        return k;
-    }();
-    if (nsplit > 65535) return SKA_ERR_UNSUPPORTED;
     if (batch > 65535 || hkv > 65535) return SKA_ERR_UNSUPPORTED;
+    if (scale == 0.f) scale = 1.0f / std::sqrt((float)d);
+    const SplitLayout L = split_layout(c->num_cus, batch, hkv, max_pages, num_splits);
+    if (L.nsplit > 65535) return SKA_ERR_UNSUPPORTED;
+    rows = (size_t)batch * num_q_heads * L.nsplit;
 
-    // workspace: [partial o | partial (m, l)]
-    const size_t po_n = (size_t)batch * num_q_heads * nsplit * d;
-    const size_t pm_n = (size_t)batch * num_q_heads * nsplit * 2;
-    const size_t off_po = 0, off_pm = off_po + align256(po_n * 4);
-    hipStream_t s = (hipStream_t)stream;
-    ska_status st = ensure_ws(c, off_pm + align256(pm_n * 4), s);
-    if (st != SKA_OK) return st;
-    if ((st = ensure_counters(c, (size_t)batch * hkv, s)) != SKA_OK) return st;
-    char *ws = (char *)c->d_ws;
-    hipEvent_t *ev = nullptr;
-    if (c->prof_n < c->prof_max) ev = &c->prof_ev[2 * (size_t)c->prof_n++];
-    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return SKA_ERR_HIP;
-
-    DecodeArgs da{};
+    da = DecodeArgs{};
     da.kcode = c->pool.kcode;
     da.page_off = c->pool.page_off;
     da.rcode = c->pool.rcode;
@@ -455,25 +464,23 @@ ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, in
     da.sin2 = c->d_sin2;
     da.scale = scale;
     da.query_mode = c->pool.query_mode;
+    da.query_f32 = c->pool.query_precision == SKA_QDIR_F32 ? 1 : 0;
     da.lut = c->d_lut;
     da.rlev = c->d_rlev;
-    da.part_o = (float *)(ws + off_po);
-    da.part_ml = (float *)(ws + off_pm);
     da.logits = logits_dbg;
     da.out = out;
     da.kdense = const_cast<uint16_t *>(k_dense);
     da.dense = k_dense != nullptr;
-    da.counters = c->d_cnt;
     da.err = c->d_err;
     da.num_pages = c->pool.num_pages;
     da.page_stride = c->page_stride;
     da.hkv = hkv;
     da.hq = num_q_heads;
     da.max_pages = max_pages;
-    da.pps = pps;
-    da.split_m = split_m;
-    da.compact = (rounds && batch <= kCompactMaxBatch) ? 1 : 0;
-    da.nsplit = nsplit;
+    da.pps = L.pps;
+    da.split_m = L.split_m;
+    da.compact = (L.rounds && batch <= kCompactMaxBatch) ? 1 : 0;
+    da.nsplit = L.nsplit;
     da.tier_mask = c->pool.tier_mask;
     da.nt = c->nt;
     for (int b = 0; b <= 8; ++b) da.tslot[b] = c->tslot[b];
@@ -481,40 +488,63 @@ ska_status decode_impl(ska_cache *c, const uint16_t *k_dense, const float *q, in
     da.app_k = app_k;
     da.app_v = app_v;
     da.tau2 = c->d_tau2;
+    return SKA_OK;
+}
+
+// One decode call on the cache's own workspace (allocated at creation).
+ska_status decode_impl(const ska_cache *c, const uint16_t *k_dense, const float *q, int batch, int num_q_heads,
+                       const int32_t *block_table, int max_pages, const int32_t *seq_lens,
+                       float scale, int num_splits, float *out, float *logits_dbg, void *stream,
+                       const float *app_k = nullptr, const uint16_t *app_v = nullptr) {
+    DecodeArgs da;
+    int G = 0;
+    size_t rows = 0;
+    ska_status st = prepare_decode(c, k_dense, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale,
+                                   num_splits, out, logits_dbg, app_k, app_v, da, G, rows);
+    if (st != SKA_OK || batch == 0) return st;
+    if (rows > c->ws_rows) return SKA_ERR_INVALID;   // (cannot happen within the maxima)
+    const int d = c->pool.d;
+    char *ws = (char *)c->d_ws;
+    da.part_o = (float *)ws;
+    da.part_ml = (float *)(ws + ws_off_ml(c->ws_rows, d));
+    da.counters = c->d_cnt;
+    hipStream_t s = (hipStream_t)stream;
+    // calls share the workspace: one on another stream waits for the last
+    if (s != c->last_stream) {
+        if (hipEventRecord(c->order_ev, c->last_stream) != hipSuccess) return SKA_ERR_HIP;
+        if (hipStreamWaitEvent(s, c->order_ev, 0) != hipSuccess) return SKA_ERR_HIP;
+        c->last_stream = s;
+    }
+    hipEvent_t *ev = nullptr;
+    if (c->prof_n < c->prof_max) ev = const_cast<hipEvent_t *>(&c->prof_ev[2 * (size_t)c->prof_n++]);
+    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return SKA_ERR_HIP;
     if (launch_decode(da, d, G, batch, s) != hipSuccess) return SKA_ERR_HIP;
     if (ev && hipEventRecord(ev[1], s) != hipSuccess) return SKA_ERR_HIP;
-
     return SKA_OK;
 }
 
 }  // namespace
 
-ska_status ska_decode_attention(ska_cache *c, const float *q, int batch, int num_q_heads,
+ska_status ska_decode_attention(const ska_cache *c, const float *q, int batch, int num_q_heads,
                                 const int32_t *block_table, int max_pages, const int32_t *seq_lens,
                                 float scale, int num_splits, float *out, float *logits_dbg, void *stream) {
     return decode_impl(c, nullptr, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale, num_splits,
                        out, logits_dbg, stream);
 }
 
-ska_status ska_append_decode_attention(ska_cache *c, const float *new_keys, const uint16_t *new_values,
+ska_status ska_append_decode_attention(const ska_cache *c, const float *new_keys, const uint16_t *new_values,
                                        const float *q, int batch, int num_q_heads, const int32_t *block_table,
                                        int max_pages, const int32_t *seq_lens, float scale, int num_splits,
                                        float *out, float *logits_dbg, void *stream) {
     if (!c) return SKA_ERR_INVALID;
-    if (batch > 0 && (!new_keys || !new_values || !block_table || !seq_lens)) return SKA_ERR_INVALID;
-    if (batch < 0 || max_pages < 1) return SKA_ERR_INVALID;
-    // the decode's own checks first, so that a rejected call writes nothing
-    if (num_q_heads < 1 || num_q_heads % c->pool.num_kv_heads != 0 || num_splits < 0) return SKA_ERR_INVALID;
-    const int G = num_q_heads / c->pool.num_kv_heads;
-    if (G != 1 && G != 2 && G != 4) return SKA_ERR_UNSUPPORTED;
-    if (!std::isfinite(scale) || scale < 0.f) return SKA_ERR_INVALID;
-    if (batch > 0 && (!q || !out)) return SKA_ERR_INVALID;
-    if (batch > 65535 || (int64_t)batch * num_q_heads > (1ll << 30)) return SKA_ERR_UNSUPPORTED;
+    if (batch > 0 && (!new_keys || !new_values)) return SKA_ERR_INVALID;
+    // (every other argument is checked by the decode before it launches
+    // anything, so a rejected call stores nothing)
     return decode_impl(c, nullptr, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale, num_splits,
                        out, logits_dbg, stream, new_keys, new_values);
 }
 
-ska_status ska_dense_decode_attention(ska_cache *c, const uint16_t *k_dense, const float *q, int batch,
+ska_status ska_dense_decode_attention(const ska_cache *c, const uint16_t *k_dense, const float *q, int batch,
                                       int num_q_heads, const int32_t *block_table, int max_pages,
                                       const int32_t *seq_lens, float scale, int num_splits, float *out,
                                       float *logits_dbg, void *stream) {
@@ -614,7 +644,7 @@ ska_status ska_rdr_plan(const ska_rdr_params *p, const float *utility, const flo
     return SKA_OK;
 }
 
-ska_status ska_decompress_keys(ska_cache *c, const int32_t *block_table, int batch, int max_pages,
+ska_status ska_decompress_keys(const ska_cache *c, const int32_t *block_table, int batch, int max_pages,
                                const int32_t *seq_lens, uint16_t *k_dense, void *stream) {
     if (!c || batch < 0 || max_pages < 1) return SKA_ERR_INVALID;
     if (batch == 0) return SKA_OK;

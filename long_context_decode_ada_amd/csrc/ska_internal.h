@@ -117,6 +117,7 @@ struct DecodeArgs {
     int8_t tslot[9];         // tier b -> index among the tiers present
     float scale;             // softmax scale
     int query_mode;          // 0: coded query, 1: exact query direction
+    int query_f32;           // query direction in f_b: 0 binary16, 1 binary32
     // decode step with append (else NULL): the new token of each sequence,
     // stored at position seq_lens[s] - 1 before that page is read
     const float *app_k;      // [B][hkv][d]

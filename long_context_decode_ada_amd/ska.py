@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libska.so")
 SKA_OK, SKA_ERR_INVALID, SKA_ERR_UNSUPPORTED, SKA_ERR_HIP, SKA_ERR_NOMEM = range(5)
 RADIUS_UNIFORM, RADIUS_LOG = 0, 1
 Q_CODED, Q_EXACT = 0, 1
+QDIR_F16, QDIR_F32 = 0, 1
 PAGE = 16
 DEVERR_SLOT, DEVERR_PAGE, DEVERR_TIER = 1, 2, 4
 
@@ -49,6 +50,11 @@ class PoolDesc(ctypes.Structure):
         ("v", ctypes.c_void_p),
         ("page_bits", ctypes.c_void_p),
         ("head_tiers", ctypes.c_int),
+        ("query_precision", ctypes.c_int),
+        ("max_batch", ctypes.c_int),
+        ("max_heads_q", ctypes.c_int),
+        ("max_pages", ctypes.c_int),
+        ("max_splits", ctypes.c_int),
     ]
 
 
@@ -132,14 +138,21 @@ def _check(s: int, what: str):
 
 
 class DevicePools:
-    """Caller-owned device pools in the library's layout (torch tensors)."""
+    """Caller-owned device pools in the library's layout (torch tensors), with
+    the maxima of the decode calls the cache built on them will serve (they
+    size its workspace, allocated once when the cache is created)."""
 
     def __init__(self, *, d: int, hkv: int, num_pages: int, tier_mask: int, radius_mode: int,
                  page_bits: torch.Tensor, kcode_bytes: int, page_off: Optional[torch.Tensor] = None,
-                 query_mode: int = Q_CODED, device="cuda", poison: bool = True, head_tiers: bool = False):
+                 query_mode: int = Q_CODED, device="cuda", poison: bool = True, head_tiers: bool = False,
+                 query_precision: int = QDIR_F16, max_batch: int = 1, max_heads_q: int = 0, max_pages: int = 1,
+                 max_splits: int = 0):
         self.d, self.hkv, self.num_pages = d, hkv, num_pages
         self.head_tiers = bool(head_tiers)
         self.tier_mask, self.radius_mode, self.query_mode = tier_mask, radius_mode, query_mode
+        self.query_precision = query_precision
+        self.max_batch, self.max_pages, self.max_splits = max_batch, max_pages, max_splits
+        self.max_heads_q = max_heads_q or 4 * hkv
         self.page_bits = page_bits.to(device=device, dtype=torch.uint8).contiguous()
         self.page_off = None if page_off is None else page_off.to(device=device, dtype=torch.int64).contiguous()
         fill = 0xFF if poison else 0
@@ -149,18 +162,25 @@ class DevicePools:
         self.v = torch.full((num_pages * hkv * d * PAGE,), 0x7FC0 if poison else 0, dtype=torch.int16, device=device)
 
     @classmethod
-    def for_workload(cls, w, device="cuda", poison=True, query_mode=Q_CODED):
+    def for_workload(cls, w, device="cuda", poison=True, query_mode=Q_CODED, query_precision=QDIR_F16,
+                     max_batch=None, max_heads_q=None, max_pages=None, max_splits=64):
+        """Pools for workload w; decode calls up to w's batch, query heads
+        and block-table width (or the given maxima), and explicit split
+        counts up to max_splits."""
         off = None if w.page_off is None else torch.from_numpy(w.page_off.view(np.int64))
         return cls(d=w.d, hkv=w.hkv, num_pages=w.num_pages, tier_mask=w.tier_mask, radius_mode=w.radius_mode,
                    page_bits=torch.from_numpy(w.page_bits), kcode_bytes=w.kcode_bytes, page_off=off,
-                   query_mode=query_mode, device=device, poison=poison, head_tiers=w.head_tiers)
+                   query_mode=query_mode, device=device, poison=poison, head_tiers=w.head_tiers,
+                   query_precision=query_precision, max_batch=max_batch or w.B, max_heads_q=max_heads_q or w.hq,
+                   max_pages=max_pages or w.max_pages, max_splits=max_splits)
 
     def desc(self) -> PoolDesc:
         return PoolDesc(self.d, self.hkv, PAGE, self.num_pages, self.radius_mode, 8, self.tier_mask,
                         self.query_mode, self.kcode.data_ptr(),
                         None if self.page_off is None else self.page_off.data_ptr(),
                         self.rcode.data_ptr(), self.v.data_ptr(), self.page_bits.data_ptr(),
-                        int(self.head_tiers))
+                        int(self.head_tiers), int(self.query_precision), int(self.max_batch),
+                        int(self.max_heads_q), int(self.max_pages), int(self.max_splits))
 
     def to_host(self) -> dict:
         return {"kcode": self.kcode.cpu().numpy(), "rcode": self.rcode.cpu().numpy(),

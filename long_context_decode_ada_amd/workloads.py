@@ -159,7 +159,7 @@ def _streams(idx: int, n: int = 10):
 
 
 def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool = True,
-         tiers: Optional[tuple] = None, head_tiers: bool = False) -> Workload:
+         tiers: Optional[tuple] = None, head_tiers: bool = False, outliers: int = 0) -> Workload:
     """Build one workload.  ``scale`` < 1 shrinks the context (and, for
     ragged_b64, the lengths) for oracle-sized tests; ``batch`` overrides B;
     ``data=False`` builds the page structure only (empty keys/values/query);
@@ -167,17 +167,23 @@ def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool 
     widths, drawn with equal probability (the sink page takes the widest);
     ``head_tiers`` (mixed_tiers only) draws the tier per (page, KV head)
     instead of per page (the sink page's heads all take the widest), with a
-    header and a record offset per (page, KV head).  Every part draws from
-    its own seeded stream, so the structure does not depend on ``data``."""
+    header and a record offset per (page, KV head); ``outliers`` (the
+    LogNormal-scaled workloads only) multiplies the channel scale of that
+    many channels per KV head, chosen at random, by a factor drawn uniformly
+    from [20, 50] (keys with a few outlier channels, a wide range of norms).
+    Every part draws from its own seeded stream, so the structure does not
+    depend on ``data``."""
     if name not in NAMES:
         raise KeyError(name)
     if tiers is not None and name != "mixed_tiers":
         raise ValueError("tiers applies to mixed_tiers only")
     if head_tiers and name != "mixed_tiers":
         raise ValueError("head_tiers applies to mixed_tiers only")
+    if outliers and name == "tiny":
+        raise ValueError("outliers applies to the LogNormal-scaled workloads only")
     tiers_override = tiers
     idx = NAMES.index(name)
-    r_keys, r_vals, r_q, r_len, r_pages, r_tier, r_evict, r_scale, _, _ = _streams(idx)
+    r_keys, r_vals, r_q, r_len, r_pages, r_tier, r_evict, r_scale, r_out, _ = _streams(idx)
 
     if name == "tiny":
         d, hq, hkv, B, T = 64, 1, 1, 1, 256
@@ -279,6 +285,10 @@ def make(name: str, scale: float = 1.0, batch: Optional[int] = None, data: bool 
     else:
         plain = name == "tiny"
         chan = None if plain else r_scale.lognormal(0.0, 0.5, size=(hkv, d)).astype(np.float32)
+        if outliers:
+            for g in range(hkv):
+                ch = r_out.choice(d, size=outliers, replace=False)
+                chan[g, ch] *= r_out.uniform(20.0, 50.0, size=outliers).astype(np.float32)
         pos_all = np.concatenate(pos_list) if n_tok else np.zeros(0, np.int64)
         keys = np.empty((n_tok, hkv, d), np.float32)
         values = np.empty((n_tok, hkv, d), np.uint16)

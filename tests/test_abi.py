@@ -34,7 +34,7 @@ def test_status_strings():
 def _desc(**kw):
     base = dict(d=128, num_kv_heads=8, page_size=16, num_pages=4, radius_mode=1, radius_bits=8,
                 tier_mask=1 << 4, query_mode=0, kcode=16, page_off=None, rcode=16, v=16, page_bits=16,
-                head_tiers=0)
+                head_tiers=0, query_precision=0, max_batch=4, max_heads_q=32, max_pages=8, max_splits=0)
     base.update(kw)
     return ska.PoolDesc(*[base[f] for f, _ in ska.PoolDesc._fields_])
 
@@ -61,6 +61,12 @@ def _enc(desc, n=1, keys=16, slot=16, rr=None, cache=None):
     (dict(page_bits=None), ska.SKA_ERR_INVALID),
     (dict(head_tiers=2), ska.SKA_ERR_INVALID),
     (dict(head_tiers=1), ska.SKA_ERR_INVALID),          # per-head tiers need the offsets
+    (dict(query_precision=2), ska.SKA_ERR_INVALID),
+    (dict(max_batch=0), ska.SKA_ERR_INVALID),            # the workspace maxima
+    (dict(max_heads_q=0), ska.SKA_ERR_INVALID),
+    (dict(max_heads_q=12), ska.SKA_ERR_INVALID),         # not a multiple of Hkv
+    (dict(max_pages=0), ska.SKA_ERR_INVALID),
+    (dict(max_splits=-1), ska.SKA_ERR_INVALID),
 ])
 def test_encode_rejects_bad_pool(kw, expect):
     assert _enc(_desc(**kw)) == expect
@@ -124,3 +130,61 @@ def test_binding_refuses_tensors_it_cannot_pass_through():
     with pytest.raises(ValueError):
         ska.rdr_plan(torch.zeros((2, 8)), torch.zeros((2, 8)), torch.zeros((2, 8), dtype=torch.uint8),
                      torch.zeros(2, dtype=torch.int32), torch.zeros(2, dtype=torch.int64), [4], [0.1], [100], 0.1)
+
+
+def test_decode_path_never_allocates():
+    """The decode's workspace is allocated when the cache is created: nothing
+    reachable from a decode call allocates, frees or synchronises."""
+    src = open(os.path.join(ROOT, "long_context_decode_ada_amd", "csrc", "ska_api.cpp")).read()
+    bodies = []
+    for fn in ("ska_status prepare_decode(", "ska_status decode_impl("):
+        i = src.index(fn)
+        j = src.index("\n}\n", i)
+        bodies.append(src[i:j])
+    for b in bodies:
+        for call in ("hipMalloc", "hipFree", "hipDeviceSynchronize", "hipStreamSynchronize", "hipMemset",
+                     "ensure_", "launch_zero"):
+            assert call not in b, call
+    launch = open(os.path.join(ROOT, "long_context_decode_ada_amd", "csrc", "k_decode.hip")).read()
+    i = launch.index("hipError_t launch_decode(")
+    body = launch[i:launch.index("\n}\n", i)]
+    assert "hipMalloc" not in body and "hipFree" not in body
+
+
+@pytest.mark.gpu
+def test_decode_outside_the_reserved_maxima_is_rejected():
+    """A decode call beyond the batch, query heads, block-table width or
+    explicit split count the cache was created for returns SKA_ERR_INVALID
+    and enqueues nothing; within them it runs."""
+    import numpy as np
+    import torch
+    from long_context_decode_ada_amd import workloads as W
+    w = W.make("gqa_t32k", 1 / 64, batch=3)
+    dev = "cuda"
+    pools = ska.DevicePools.for_workload(w, device=dev, max_batch=2, max_splits=4)
+    cache = ska.Cache(pools)
+    ska.encode_keys(cache, torch.from_numpy(w.keys).to(dev), torch.from_numpy(w.values.view(np.int16)).to(dev),
+                    torch.from_numpy(w.slot).to(dev))
+    q = torch.from_numpy(w.q).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    out = torch.full((3, w.hq, w.d), 7.0, device=dev)
+    with pytest.raises(ska.SkaError) as e:                 # batch 3 > 2
+        ska.decode_attention(cache, q, bt, sl, out=out)
+    assert e.value.status == ska.SKA_ERR_INVALID
+    with pytest.raises(ska.SkaError) as e:                 # 8 splits > 4
+        ska.decode_attention(cache, q[:2], bt[:2], sl[:2], num_splits=8, out=out[:2])
+    assert e.value.status == ska.SKA_ERR_INVALID
+    wide = torch.zeros((2, w.max_pages + 1), dtype=torch.int32, device=dev)
+    wide[:, : w.max_pages] = bt[:2]
+    with pytest.raises(ska.SkaError) as e:                 # a wider block table
+        ska.decode_attention(cache, q[:2], wide, sl[:2], out=out[:2])
+    assert e.value.status == ska.SKA_ERR_INVALID
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())                        # nothing ran
+    ska.decode_attention(cache, q[:2], bt[:2], sl[:2], num_splits=4, out=out[:2])
+    ska.decode_attention(cache, q[:2], bt[:2], sl[:2], out=out[:2])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out[:2]).all()) and bool((out[2] == 7.0).all())
+    assert ska.device_errors(cache) == 0
+    cache.free()

@@ -219,3 +219,25 @@ def test_multi_round_batches_past_one_wave_of_lengths(scale, batch):
     o = oracle_run(w, rng)
     assert g["errors"] == 0
     compare(w, g, o, rng, label="rounds B=%d" % batch)
+
+
+@pytest.mark.parametrize("name,scale,batch", [("gqa_t32k", 1 / 16, None), ("mixed_tiers", 1 / 16, 4)])
+def test_high_dynamic_range_keys(name, scale, batch):
+    """Keys with four outlier channels per KV head (scales x20..x50 on top of
+    the LogNormal channel scales): norms span a wide range and the logit
+    bound scale*|q|*r~ grows several-fold.  With the query direction in
+    binary16 the logits stay within their bar (their error is relative to the
+    bound) but, scaled by the large radii through a sharp softmax, move the
+    outputs by more than 2e-3; with the binary32 direction (query_precision)
+    both bars hold."""
+    from long_context_decode_ada_amd import ska
+    w = W.make(name, scale, batch=batch, outliers=4)
+    rng = O.calibrate(w.keys)
+    o = oracle_run(w, rng)
+    g = gpu_run(w, query_precision=ska.QDIR_F32)
+    for k in ("kcode", "rcode", "v"):
+        assert np.array_equal(g["pools"][k], o["pools"][k]), k
+    compare(w, g, o, rng, label="%s, outlier channels, binary32 query direction" % name)
+    g16 = gpu_run(w)
+    oe, _ = compare(w, g16, o, rng, label="%s, outlier channels, binary16 query direction" % name, out_tol=None)
+    say("   binary16 direction: output error %.3g (bar 2e-3 not required here)" % oe)

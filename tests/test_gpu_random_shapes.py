@@ -2,7 +2,8 @@
 dimension, KV heads, group size, batch, lengths (zero, page boundaries,
 odd tails), one tier or mixed tiers (fixed stride or packed pages, tiers per
 page or per (page, KV head)), radius mode, query mode and split count are
-drawn per case.  Every case checks the encode bit for bit and the decode
+drawn per case, and so is the precision of the query direction (binary16 or
+binary32).  Every case checks the encode bit for bit and the decode
 (outputs and logits) against the oracle; every other case also runs the
 decode step with append."""
 import numpy as np
@@ -71,19 +72,22 @@ def _case(seed):
                    seq_lens=lens, block_table=bt, num_pages=num_pages, page_bits=pb, page_off=off,
                    bstride=bstride, kcode_bytes=kcode_bytes, keys=keys, values=values, slot=slot, q=q,
                    head_tiers=head_tiers)
-    return w, int(r.choice([0, 1, 3, 7])), int(r.choice([0, 0, 1]))
+    splits, qmode = int(r.choice([0, 1, 3, 7])), int(r.choice([0, 0, 1]))
+    qprec = int(r.random() < 0.5)          # query direction in binary16 or binary32
+    return w, splits, qmode, qprec
 
 
 @pytest.mark.parametrize("seed", range(40))
 def test_random_shape_parity(seed):
-    w, splits, qmode = _case(seed)
-    say("[random %d] d=%d hkv=%d G=%d B=%d lens=%s tiers=%s head_tiers=%s packed=%s splits=%d query_mode=%d" %
+    w, splits, qmode, qprec = _case(seed)
+    say("[random %d] d=%d hkv=%d G=%d B=%d lens=%s tiers=%s head_tiers=%s packed=%s splits=%d query_mode=%d "
+        "query_precision=%d" %
         (seed, w.d, w.hkv, w.hq // w.hkv, w.B, w.seq_lens.tolist(), sorted(t for t in range(9) if w.tier_mask >> t & 1),
-         w.head_tiers, w.page_off is not None, splits, qmode))
+         w.head_tiers, w.page_off is not None, splits, qmode, qprec))
     if w.n_tokens == 0:
         pytest.skip("no token in this draw")
     rng = O.calibrate(w.keys)
-    g = gpu_run(w, num_splits=splits, query_mode=qmode)
+    g = gpu_run(w, num_splits=splits, query_mode=qmode, query_precision=qprec)
     assert np.array_equal(g["range"], rng)
     o = oracle_run(w, rng, query_mode=qmode)
     for k in ("kcode", "rcode", "v"):
@@ -91,14 +95,14 @@ def test_random_shape_parity(seed):
     assert g["errors"] == 0
     compare(w, g, o, rng, label="random %d" % seed)
     if seed % 2 == 0:
-        _append_check(w, rng, splits, qmode, o)
+        _append_check(w, rng, splits, qmode, qprec, o)
 
 
-def _append_check(w, rng, splits, qmode, o):
+def _append_check(w, rng, splits, qmode, qprec, o):
     import torch
     from long_context_decode_ada_amd import ska
     dev = "cuda"
-    pools = ska.DevicePools.for_workload(w, device=dev, poison=True, query_mode=qmode)
+    pools = ska.DevicePools.for_workload(w, device=dev, poison=True, query_mode=qmode, query_precision=qprec)
     cache = ska.Cache(pools)
     starts = np.concatenate([[0], np.cumsum(w.seq_lens)[:-1]]).astype(np.int64)
     last = np.where(w.seq_lens > 0, starts + w.seq_lens - 1, -1)

@@ -80,3 +80,19 @@ def test_head_tier_layout_is_packed_per_page_and_head():
         assert (hb[w.block_table[s, 0]] == 8).all()
     w0 = W.make("mixed_tiers", 1 / 64, batch=2)
     assert np.array_equal(w0.seq_lens, w.seq_lens) and np.array_equal(w0.block_table, w.block_table)
+
+
+def test_outlier_channels():
+    """Keys with a few outlier channels: seeded, and the chosen channels
+    carry norms far above the rest."""
+    a = W.make("gqa_t32k", 1 / 256, outliers=4)
+    b = W.make("gqa_t32k", 1 / 256, outliers=4)
+    assert np.array_equal(a.keys, b.keys)
+    plain = W.make("gqa_t32k", 1 / 256)
+    assert np.array_equal(a.values, plain.values) and np.array_equal(a.q, plain.q)
+    ra = np.linalg.norm(a.keys.astype(np.float64), axis=2)
+    rp = np.linalg.norm(plain.keys.astype(np.float64), axis=2)
+    assert ra.mean() > 3 * rp.mean()          # the outlier channels dominate the norms
+    assert ra.max() / ra.min() > rp.max() / rp.min()
+    with pytest.raises(ValueError):
+        W.make("tiny", outliers=2)
