@@ -178,6 +178,24 @@ ska_status ska_decode_attention(const ska_cache *cache, const float *q, int batc
                                 const int32_t *seq_lens, float scale, int num_splits,
                                 float *out, float *logits_dbg, void *stream);
 
+/* ska_decode_attention_noalloc -- for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): ska_decode_attention (without logits_dbg) with its split
+ * partials and merge counters in a static device array of the library
+ * (16 MiB per GPU, kept until the process ends) instead of the cache's
+ * workspace.  Allocates nothing and frees nothing; the first call on a GPU
+ * looks the array up and clears its counters with a small kernel on
+ * `stream`.  Rejects with SKA_ERR_INVALID, before enqueueing anything, a
+ * call whose partials (batch * num_q_heads * splits rows of (d + 2) floats)
+ * exceed 16 MiB - 256 KiB or whose batch * Hkv exceeds 65536, and anything
+ * ska_decode_attention rejects.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on the device (different streams, not ordered
+ * by the caller) race and give wrong results.  Results equal
+ * ska_decode_attention's. */
+ska_status ska_decode_attention_noalloc(const ska_cache *cache, const float *q, int batch, int num_q_heads,
+                                        const int32_t *block_table, int max_pages, const int32_t *seq_lens,
+                                        float scale, int num_splits, float *out, void *stream);
+
 /* ska_append_decode_attention -- a decode step that first stores the step's
  * new token (the write path of section 2.3, dense key -> spherical codes ->
  * paged store, run inside the step), then decodes over all tokens including

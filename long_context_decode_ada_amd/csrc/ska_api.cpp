@@ -18,6 +18,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -524,6 +525,75 @@ ska_status decode_impl(const ska_cache *c, const uint16_t *k_dense, const float 
 }
 
 }  // namespace
+
+// ---- the decode for callers that cannot allocate ----
+//
+// ska_decode_attention_noalloc keeps its split partials and merge counters in
+// this file-scope device array instead of the cache's workspace: one copy per
+// GPU, held until the process ends.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in): the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address reaches kernels.
+namespace {
+constexpr size_t kScratchBytes = (size_t)16 << 20;                  // 16 MiB per GPU
+constexpr size_t kScratchCounters = 65536;                          // (sequence, KV head) merge counters
+constexpr size_t kScratchCounterBytes = kScratchCounters * sizeof(uint32_t);
+constexpr size_t kScratchPartialBytes = kScratchBytes - kScratchCounterBytes;
+constexpr int kScratchMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+char *g_scratch[kScratchMaxDevices];   // device address of each GPU's copy (nullptr: not yet set up)
+
+// The device address of `device`'s scratch array; on the first call for that
+// device it is looked up (with the device current) and its merge counters
+// are cleared on `s` by a fill kernel (every completed call leaves the
+// counters it used at zero again).
+ska_status scratch_base(int device, hipStream_t s, char **out) {
+    if (device < 0 || device >= kScratchMaxDevices) return SKA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[device]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return SKA_ERR_HIP;
+        if (cur != device && hipSetDevice(device) != hipSuccess) return SKA_ERR_HIP;
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e == hipSuccess && !p) e = hipErrorInvalidSymbol;
+        if (e == hipSuccess) e = launch_zero_u32(static_cast<uint32_t *>(p), (int64_t)kScratchCounters, s);
+        if (cur != device) (void)hipSetDevice(cur);
+        if (e != hipSuccess) return SKA_ERR_HIP;
+        g_scratch[device] = static_cast<char *>(p);
+    }
+    *out = g_scratch[device];
+    return SKA_OK;
+}
+}  // namespace
+
+ska_status ska_decode_attention_noalloc(const ska_cache *c, const float *q, int batch, int num_q_heads,
+                                        const int32_t *block_table, int max_pages, const int32_t *seq_lens,
+                                        float scale, int num_splits, float *out, void *stream) {
+    DecodeArgs da;
+    int G = 0;
+    size_t rows = 0;
+    ska_status st = prepare_decode(c, nullptr, q, batch, num_q_heads, block_table, max_pages, seq_lens, scale,
+                                   num_splits, out, nullptr, nullptr, nullptr, da, G, rows);
+    if (st != SKA_OK || batch == 0) return st;
+    const int d = c->pool.d;
+    // beyond the scratch array: rejected before anything is enqueued
+    if ((size_t)batch * c->pool.num_kv_heads > kScratchCounters || ws_bytes(rows, d) > kScratchPartialBytes)
+        return SKA_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = nullptr;
+    if ((st = scratch_base(c->device, s, &base)) != SKA_OK) return st;
+    da.counters = reinterpret_cast<uint32_t *>(base);
+    da.part_o = reinterpret_cast<float *>(base + kScratchCounterBytes);
+    da.part_ml = reinterpret_cast<float *>(base + kScratchCounterBytes + ws_off_ml(rows, d));
+    if (launch_decode(da, d, G, batch, s) != hipSuccess) return SKA_ERR_HIP;
+    return SKA_OK;
+}
 
 ska_status ska_decode_attention(const ska_cache *c, const float *q, int batch, int num_q_heads,
                                 const int32_t *block_table, int max_pages, const int32_t *seq_lens,

@@ -23,7 +23,8 @@ QDIR_F16, QDIR_F32 = 0, 1
 PAGE = 16
 DEVERR_SLOT, DEVERR_PAGE, DEVERR_TIER = 1, 2, 4
 
-SYMBOLS = ("ska_encode_keys", "ska_decode_attention", "ska_append_decode_attention", "ska_dense_decode_attention",
+SYMBOLS = ("ska_encode_keys", "ska_decode_attention", "ska_decode_attention_noalloc", "ska_append_decode_attention",
+           "ska_dense_decode_attention",
            "ska_decompress_keys", "ska_rdr_plan", "ska_get_radius_range", "ska_device_errors",
            "ska_profile_begin", "ska_profile_read", "ska_free", "ska_status_string")
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.ska_encode_keys.argtypes = [ctypes.POINTER(P), ctypes.POINTER(PoolDesc), P, P, P, i64, P, P]
         L.ska_decode_attention.restype = i
         L.ska_decode_attention.argtypes = [P, P, i, i, P, i, P, f, i, P, P, P]
+        L.ska_decode_attention_noalloc.restype = i
+        L.ska_decode_attention_noalloc.argtypes = [P, P, i, i, P, i, P, f, i, P, P]
         L.ska_append_decode_attention.restype = i
         L.ska_append_decode_attention.argtypes = [P, P, P, P, i, i, P, i, P, f, i, P, P, P]
         L.ska_dense_decode_attention.restype = i
@@ -254,6 +257,22 @@ def decode_attention(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, s
                                    _ptr(seq_lens), float(scale), int(num_splits), _ptr(out), _ptr(logits),
                                    _stream(stream))
     _check(s, "ska_decode_attention")
+    return out
+
+
+def decode_attention_noalloc(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                             scale: float = 0.0, num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """ska_decode_attention_noalloc: decode_attention with the split workspace in the library's static
+    device array (nothing allocated by the library; `out` must be given by a caller that cannot allocate)."""
+    B, hq, d = q.shape
+    _decode_checks(cache, q, block_table, seq_lens, out, None)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    s = lib().ska_decode_attention_noalloc(cache.handle, _ptr(q), B, hq, _ptr(block_table),
+                                           int(block_table.shape[1]), _ptr(seq_lens), float(scale), int(num_splits),
+                                           _ptr(out), _stream(stream))
+    _check(s, "ska_decode_attention_noalloc")
     return out
 
 
