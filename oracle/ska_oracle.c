@@ -345,7 +345,13 @@ void ora_unpack(const uint8_t *rec, int d, int b, int32_t *codes)
 /* ------------------------------------------------------------------------ */
 /* Paged pools (format choice; [SKV 1] paged KV substrate, [SKV 2.2]
  * tier-homogeneous pages with a header, [SKV 2.3] vLLM-style layouts).
- *   page_bits[phys]         : angle bits b of every key in the page (header)
+ *   page_bits[phys]         : the page header: angle bits b of every key in
+ *                             the page in the low four bits; in the high four
+ *                             bits the number of empty slots at the end of the
+ *                             page (0: all 16 slots hold tokens), so that a
+ *                             page may hold fewer than 16 retained tokens
+ *                             anywhere in a row ([SKV 2.2]: retained states
+ *                             grouped into tier-homogeneous pages)
  *   kcode + base(phys)      : [hkv][16 tokens][KB(b)] records;
  *                             base = page_off[phys] if page_off != NULL,
  *                             else phys * hkv * 16 * KB(bstride)
@@ -363,10 +369,21 @@ static size_t page_base(int64_t phys, int hkv, int d, const uint64_t *page_off, 
     return (size_t)phys * (size_t)hkv * ORA_PAGE * (size_t)ora_kb(d, bstride);
 }
 
+static int header_of(const uint8_t *page_bits, int head_tiers, int64_t phys, int hkv, int g)
+{
+    return head_tiers ? page_bits[(size_t)phys * hkv + g] : page_bits[phys];
+}
+
 /* tier of KV head g's records in page phys */
 static int tier_of(const uint8_t *page_bits, int head_tiers, int64_t phys, int hkv, int g)
 {
-    return head_tiers ? page_bits[(size_t)phys * hkv + g] : page_bits[phys];
+    return header_of(page_bits, head_tiers, phys, hkv, g) & 15;
+}
+
+/* slots of page phys (KV head g) that hold tokens: slots 0 .. count-1 */
+static int count_of(const uint8_t *page_bits, int head_tiers, int64_t phys, int hkv, int g)
+{
+    return ORA_PAGE - (header_of(page_bits, head_tiers, phys, hkv, g) >> 4);
 }
 
 /* byte offset of the record of (page phys, KV head g, slot), kb bytes each */
@@ -443,8 +460,9 @@ static double bf16_to_double(uint16_t h)
 
 /* ------------------------------------------------------------------------ */
 /* ADA decode, plain definition [SKV 2.1]: for sequence s and query head h
- * (KV head g = h / (hq/hkv)), over the n = seq_lens[s] resident tokens
- * t (page t/16 of the block table, slot t%16):
+ * (KV head g = h / (hq/hkv)), over the resident tokens t < n = seq_lens[s]
+ * (page t/16 of the block table, slot t%16, resident when the slot is below
+ * the page's token count from its header):
  *   l_t = scale * |q| * r~_t * <u_q, u_t>
  * with u_t the decoded direction of the key's codes, r~_t its radius level,
  * and u_q the decoded direction of the query's own codes at the page's tier
@@ -453,8 +471,9 @@ static double bf16_to_double(uint16_t h)
  * are reconstructed here in host memory ("decompress-then-dot", [SKV 1]),
  * which is the slow definition that ADA reaches without materialising them.
  * out [B][hq][d] fp32; logits [B][hq][max_pages*16] fp32 or NULL (natural
- * units, at logical token positions); pairs = list of (s, h) to compute, or
- * NULL for all.  Returns 0, or 1 on a bad argument. */
+ * units, at logical positions 16*p + slot of the resident tokens); pairs =
+ * list of (s, h) to compute, or NULL for all.  A row with no resident token
+ * gets a zero output.  Returns 0, or 1 on a bad argument. */
 int ora_decode(int d, int hkv, int radius_mode, const double *range,
                const uint8_t *page_bits, const uint64_t *page_off, int bstride, int head_tiers,
                const uint8_t *kcode, const uint8_t *rcode, const uint16_t *v,
@@ -505,9 +524,15 @@ int ora_decode(int d, int hkv, int radius_mode, const double *range,
         double qn = sqrt(qT);
         double *l = malloc(sizeof(double) * (size_t)n);
         double *u = malloc(sizeof(double) * (size_t)d);
+        char *res = malloc((size_t)n);
+        int nres = 0;
         for (int t = 0; t < n; ++t) {
             int64_t phys = block_table[(size_t)s * max_pages + t / ORA_PAGE];
             int slot = t % ORA_PAGE;
+            res[t] = slot < count_of(page_bits, head_tiers, phys, hkv, g);
+            if (!res[t])
+                continue;
+            ++nres;
             int b = tier_of(page_bits, head_tiers, phys, hkv, g);
             if (b < 1 || b > 8) {
                 bad = 1;
@@ -535,13 +560,23 @@ int ora_decode(int d, int hkv, int radius_mode, const double *range,
             if (logits)
                 logits[((size_t)s * hq + h) * (size_t)max_pages * ORA_PAGE + t] = (float)l[t];
         }
-        double m = l[0];
-        for (int t = 1; t < n; ++t)
-            if (l[t] > m)
+        if (nres == 0) {
+            for (int e = 0; e < d; ++e)
+                o[e] = 0.0f;
+            free(res);
+            free(l);
+            free(u);
+            continue;
+        }
+        double m = -INFINITY;
+        for (int t = 0; t < n; ++t)
+            if (res[t] && l[t] > m)
                 m = l[t];
         double den = 0.0;
         double *num = calloc((size_t)d, sizeof(double));
         for (int t = 0; t < n; ++t) {
+            if (!res[t])
+                continue;
             double w = exp(l[t] - m);
             int64_t phys = block_table[(size_t)s * max_pages + t / ORA_PAGE];
             int slot = t % ORA_PAGE;
@@ -552,6 +587,7 @@ int ora_decode(int d, int hkv, int radius_mode, const double *range,
         for (int e = 0; e < d; ++e)
             o[e] = (float)(num[e] / den);
         free(num);
+        free(res);
         free(l);
         free(u);
     }
@@ -786,8 +822,11 @@ int ora_rdr_plan(int n, const float *u, const float *knorm, const uint8_t *prot,
             ++cnt;
         }
         int np = (cnt + ORA_PAGE - 1) / ORA_PAGE;
-        for (int p = 0; p < np; ++p)
-            page_tier[page + p] = (uint8_t)tiers[k];
+        for (int p = 0; p < np; ++p) {
+            /* the header: the tier, and for the tier's last page its empty slots */
+            int empty = (p == np - 1) ? np * ORA_PAGE - cnt : 0;
+            page_tier[page + p] = (uint8_t)(tiers[k] | (empty << 4));
+        }
         page += np;
     }
     *npages = page;
