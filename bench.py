@@ -89,9 +89,13 @@ def cpu_baseline(w, nseq: int, min_seconds: float):
     import numpy as np
     from long_context_decode_ada_amd import workloads as W
     from oracle import oracle as O
+    # the first nseq sequences (their keys are the first rows of w.keys)
+    sub = W.Workload(**{**w.__dict__, "B": nseq, "seq_lens": w.seq_lens[:nseq], "block_table": w.block_table[:nseq],
+                        "q": w.q[:nseq]})
+    ntok = sub.n_tokens
     rng = O.calibrate(w.keys)
     pools = W.host_pools(w, poison=False)
-    rows = slice(0, int(w.seq_lens[:nseq].astype(np.int64).sum()))
+    rows = slice(0, ntok)
     O.encode(pools, w.keys[rows], w.values[rows], w.slot[rows], w.radius_mode, rng)
     pairs = [(s, h) for s in range(nseq) for h in range(w.hq)]
     reps, t0 = 0, time.perf_counter()
@@ -101,10 +105,7 @@ def cpu_baseline(w, nseq: int, min_seconds: float):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= 100:
             break
-    ntok = int(w.seq_lens[:nseq].sum())
-    per_tok = W.record_bytes(w.d, int(w.page_bits[w.block_table[0, 0]])) + 1 + 2 * w.d
-    npg = sum((int(w.seq_lens[s]) + 15) // 16 for s in range(nseq))
-    nbytes = reps * (ntok * w.hkv * per_tok + npg * w.hkv * 5)
+    nbytes = reps * (sub.bytes_per_step() - nseq * w.hq * w.d * 8)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": O.max_threads(), "kind": "oracle",
             "kv_tokens_per_s": reps * ntok / dt, "seconds": dt,
             "sample": "%d of %d sequences of %s (%d tokens, all %d query heads), decode only, %d passes" %
@@ -208,7 +209,19 @@ def main():
     from long_context_decode_ada_amd import workloads as W
 
     t0 = time.time()
-    w = W.make(args.workload, head_tiers=args.head_tiers)
+    if args.workload == "mixed_tiers_rdr":
+        # tiers and evictions planned by the library's RDR controller
+        inp = W.rdr_inputs()
+        plan = ska.rdr_plan(*(torch.from_numpy(a).to("cuda") for a in (inp.utility, inp.key_norm, inp.protect,
+                                                                          inp.num_states, inp.budget)),
+                            inp.tiers, inp.eps, inp.bytes_per_tier, inp.sigma)
+        plan = {k: v.cpu().numpy() for k, v in plan.items()}
+        w = W.planned_workload(inp, plan["tier"], plan["page"], plan["slot"],
+                               [plan["page_tier"][s, : int(plan["npages"][s])] for s in range(inp.base.B)],
+                               plan["npages"])
+        del inp
+    else:
+        w = W.make(args.workload, head_tiers=args.head_tiers)
     log("workload %s: B=%d hq=%d hkv=%d d=%d tokens=%d pages=%d (%.1fs)" %
         (w.name, w.B, w.hq, w.hkv, w.d, w.n_tokens, w.num_pages, time.time() - t0))
     dev = "cuda"

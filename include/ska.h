@@ -27,7 +27,11 @@
  *            [R_lo, R_hi], rounded at the (linear or log) midpoint.
  *   record   KB(b) = 16*ceil((d-1)*b/128) bytes per key, four equal slices;
  *            slice s holds angles [s*d/4, (s+1)*d/4) LSB-first, rest zero.
- *   pools    page_bits[phys] (uint8)        tier b of the page
+ *   pools    page_bits[phys] (uint8)        page header: tier b of the page in
+ *                                           the low four bits; the number of
+ *                                           empty slots at the page's end in
+ *                                           the high four (0: 16 tokens), so
+ *                                           any page of a row may be partial
  *            kcode + base(phys)             [Hkv][16][KB(b)] records,
  *                                           base = page_off[phys] or
  *                                           phys*Hkv*16*KB(b_max of mask)
@@ -153,8 +157,10 @@ ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool,
  * logit estimator, section 2.2 header-guided page streaming): for sequence s
  * and query head h (KV head h / (Hq/Hkv)), the logits
  *     l_t = scale * |q| * r~_t * f_b(c_q, c_t)
- * over the seq_lens[s] resident tokens (token t at page t/16 of row s of
- * the block table, slot t%16), then softmax and the value-weighted sum.
+ * over the resident tokens of row s: position t < seq_lens[s] is page t/16
+ * of row s of the block table, slot t%16, and holds a token when that slot
+ * is below the page's count (its header); then softmax over them and the
+ * value-weighted sum.
  *   q            device fp32 [batch][num_q_heads][d]
  *   block_table  device int32 [batch][max_pages]
  *   seq_lens     device int32 [batch] (0 gives a zero output row)
@@ -168,7 +174,8 @@ ska_status ska_encode_keys(ska_cache **cache, const ska_pool_desc *pool,
  *                first.  Results agree across split counts to rounding.
  *   out          device fp32 [batch][num_q_heads][d]
  *   logits_dbg   device fp32 [batch][num_q_heads][max_pages*16] or NULL;
- *                receives l_t (natural units) at each resident position
+ *                receives l_t (natural units) at each resident position t
+ *                (other positions are left as they are)
  *                (the same kernel as without it, plus the logit stores)
  * Hq/Hkv must be 1, 2 or 4.  batch, num_q_heads, max_pages and an explicit
  * num_splits must lie within the cache's declared maxima (else
@@ -282,7 +289,10 @@ typedef struct {
  *   tier_out   uint8 [batch][max_states]: 0 = evicted, else the tier's width
  *   page_out, slot_out  int32 [batch][max_states]: page and slot of each
  *              retained state, -1 when evicted
- *   page_tier_out  uint8 [batch][max_pages_out]: width of each page;
+ *   page_tier_out  uint8 [batch][max_pages_out]: the header of each page
+ *              (page_bits format: the width in the low four bits; each tier's
+ *              last page has its empty slots in the high four), so a row of
+ *              the planned pages decodes as one sequence;
  *              max_pages_out >= ceil(max_states/16) + ntiers
  *   npages_out int32 [batch], lambda_out double [batch],
  *   status_out int32 [batch]: 0, or 2 when the protected states alone exceed

@@ -63,7 +63,7 @@ __device__ void encode_one(const EncodeArgs &A, const float *__restrict__ x, con
         atomicOr(A.err, 1u);
         return;
     }
-    const int b = A.page_bits[A.head_tiers ? phys * A.hkv + g : phys];
+    const int b = A.page_bits[A.head_tiers ? phys * A.hkv + g : phys] & 15;   // (the header's tier bits)
     if (b < 1 || b > 8 || !((A.tier_mask >> b) & 1u)) {
         atomicOr(A.err, 4u);
         return;

@@ -278,6 +278,8 @@ struct PageBuf {
 // Wave-uniform description of one page.
 struct PageDesc {
     int phys, b, p;
+    int cnt;        // slots holding tokens (header-dispatched pages; single-tier kernels
+                    // read the count from the header loaded with the page)
     uint64_t off;   // byte offset of the physical page's code block
     bool live;      // false: the loads go through empty descriptors and read nothing
 };
@@ -606,18 +608,23 @@ __device__ __forceinline__ void compute_page(const DecodeArgs &A, const PageDesc
                                              const uint32_t (&qd)[D / 4], float sq,
                                              const float2 *__restrict__ lut, const float *__restrict__ rlev,
                                              float *__restrict__ pb, WaveState &st, v4f (&acc)[D / 16]) {
-    const int ntok = min(kPage, len - pd.p * kPage);
+    // tokens of the page: its first slots, up to the row's length and (coded
+    // pools) the header's count (the high four bits count empty slots)
+    int ntok = min(kPage, len - pd.p * kPage);
     const int64_t lbase = head0 * A.max_pages * kPage + (int64_t)pd.p * kPage;
     if constexpr (TB == kDenseTB) {
         compute_page_dense<D, G, DBG>(A, r, ntok, lbase, qd, sq, pb, st, acc);
     } else if constexpr (TB != 0) {
         // a page whose header disagrees with the kernel's tier is flagged and skipped
-        if (__builtin_amdgcn_readfirstlane(r.hb) != TB) {
+        const uint32_t hb = __builtin_amdgcn_readfirstlane(r.hb);
+        if ((hb & 15u) != (uint32_t)TB) {
             if ((threadIdx.x & 63) == 0) atomicOr(A.err, 4u);
             return;
         }
+        ntok = min(ntok, kPage - (int)(hb >> 4));
         compute_page_b<D, G, TB, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc);
     } else {
+        ntok = min(ntok, pd.cnt);
         switch (pd.b) {
             case 2: compute_page_b<D, G, 2, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
             case 3: compute_page_b<D, G, 3, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
@@ -669,7 +676,7 @@ __device__ __forceinline__ void append_token(const DecodeArgs &A, int seq, int k
     // (the header is read now and checked before the stores; with a single
     // tier the codes need not wait for it)
     const int64_t hix = A.head_tiers ? (int64_t)ph * A.hkv + kvh : (int64_t)ph;
-    const int hb = A.page_bits[hix];
+    const int hb = A.page_bits[hix] & 15;   // (the tier bits of the header)
     const int b = TB != 0 ? TB : hb;
     if (TB == 0 && !(b >= 2 && b <= 8 && ((A.tier_mask >> b) & 1u))) {
         if (lane == 0) atomicOr(A.err, 4u);
@@ -978,12 +985,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             // per-head tiers), read at a clamped (valid) id
             const int phc = ok ? ph : 0;
             const int64_t hix = A.head_tiers ? (int64_t)phc * A.hkv + kvh : (int64_t)phc;
-            const int bb = (int)A.page_bits[hix];
+            const int hdr = (int)A.page_bits[hix];
+            const int bb = hdr & 15;   // tier bits; the high four count empty slots
             const uint64_t off = A.page_off ? A.page_off[hix] : (uint64_t)phc * (uint64_t)A.page_stride;
             const bool okb = ok && bb >= 2 && bb <= 8 && ((A.tier_mask >> bb) & 1u);
             if (ok && !okb) atomicOr(A.err, 4u);
             e_phys = okb ? ph : -1;
-            e_bits = okb ? bb : 0;
+            e_bits = okb ? hdr : 0;
             key = okb ? bb : 15;
             e_lo = okb ? (uint32_t)off : 0u;
             e_hi = okb ? (uint32_t)(off >> 32) : 0u;
@@ -1012,7 +1020,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     auto desc = [&](int k) {
         PageDesc pd;
         pd.phys = __builtin_amdgcn_readlane(e_phys, k);
-        pd.b = TB != 0 ? TB : __builtin_amdgcn_readlane(e_bits, k);
+        const int hdr = TB != 0 ? TB : __builtin_amdgcn_readlane(e_bits, k);
+        pd.b = hdr & 15;
+        pd.cnt = kPage - (hdr >> 4);
         pd.p = __builtin_amdgcn_readlane(e_pg, k);
         pd.live = true;
         if constexpr (TB != 0) {
@@ -1065,6 +1075,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         pd.live = ok && k < nw;
         pd.phys = ok ? ph : 0;
         pd.b = TB != 0 ? TB : 8;
+        pd.cnt = kPage;   // (single tier: the count comes with the page's header)
         pd.p = wp0 + kc;
         pd.off = (uint64_t)(uint32_t)pd.phys * (uint64_t)A.page_stride;
         if (!ok && k < nw && lane == 0) atomicOr(A.err, 2u);

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void k_decompress(DecodeArgs A) {
         btv = A.block_table[(int64_t)seq * A.max_pages + p0 + kWaves * lane];
         if (TB == 0 && (uint32_t)btv < npg32) {
             const int64_t hix = A.head_tiers ? (int64_t)btv * A.hkv + kvh : (int64_t)btv;
-            hbv = A.page_bits[hix];
+            hbv = A.page_bits[hix] & 15;   // (the tier bits of the header)
             offv = A.page_off ? A.page_off[hix] : (uint64_t)btv * (uint64_t)A.page_stride;
         }
     }
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void k_decompress(DecodeArgs A) {
     auto emit = [&](const Pg &g) {
         bool st = g.live;
         if (TB != 0) {
-            const bool hdr_ok = __builtin_amdgcn_readfirstlane(g.hb) == TB;
+            const bool hdr_ok = (__builtin_amdgcn_readfirstlane(g.hb) & 15u) == (uint32_t)TB;
             err |= (g.live && !hdr_ok) ? 4u : 0u;
             st = g.live && hdr_ok;
         }

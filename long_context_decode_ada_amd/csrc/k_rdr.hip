@@ -360,9 +360,12 @@ __global__ __launch_bounds__(kRdrThreads) void k_rdr_pack(RdrArgs A) {
             ++pos;
         }
         const int np = (total + 15) / 16;
+        // page headers: the tier, and on the tier's last page its empty slots
         if (blockIdx.x == 0)
             for (int p = threadIdx.x; p < np; p += kRdrThreads)
-                if (page + p < A.max_pages_out) A.page_tier[(int64_t)c.seq * A.max_pages_out + page + p] = tk;
+                if (page + p < A.max_pages_out)
+                    A.page_tier[(int64_t)c.seq * A.max_pages_out + page + p] =
+                        (uint8_t)(tk | ((p == np - 1 ? np * 16 - total : 0) << 4));
         page += np;
     }
     for (int i = j0; i < j1; ++i) {

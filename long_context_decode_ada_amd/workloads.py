@@ -67,7 +67,8 @@ class Workload:
     seq_lens: np.ndarray            # int32 [B] resident tokens
     block_table: np.ndarray         # int32 [B][max_pages]
     num_pages: int
-    page_bits: np.ndarray           # uint8 [num_pages] ([num_pages*hkv] with head_tiers)
+    page_bits: np.ndarray           # uint8 [num_pages] ([num_pages*hkv] with head_tiers): tier in the low
+                                    # four bits, empty slots at the page's end in the high four
     page_off: Optional[np.ndarray]  # uint64 [num_pages] ([num_pages*hkv] with head_tiers) or None
     bstride: int                    # tier used for the fixed page stride when page_off is None
     kcode_bytes: int
@@ -85,7 +86,18 @@ class Workload:
 
     @property
     def n_tokens(self) -> int:
-        return int(self.seq_lens.astype(np.int64).sum())
+        """Resident tokens: positions below each row's length, less the empty
+        slots page headers declare."""
+        if not np.any(np.asarray(self.page_bits) >> 4):
+            return int(self.seq_lens.astype(np.int64).sum())
+        tot = 0
+        for s in range(self.B):
+            n = int(self.seq_lens[s])
+            for p in range((n + PAGE - 1) // PAGE):
+                phys = int(self.block_table[s, p])
+                hdr = int(self.page_bits[phys * self.hkv] if self.head_tiers else self.page_bits[phys])
+                tot += min(PAGE - (hdr >> 4), n - p * PAGE)
+        return tot
 
     def bytes_per_step(self) -> int:
         """Algorithmic HBM bytes of one decode step: per resident (token, kv
@@ -98,10 +110,11 @@ class Workload:
             npg = (n + PAGE - 1) // PAGE
             for p in range(npg):
                 phys = int(self.block_table[s, p])
-                ntok = min(PAGE, n - p * PAGE)
                 for g in range(self.hkv):
-                    b = int(self.page_bits[phys * self.hkv + g] if self.head_tiers else self.page_bits[phys])
-                    tot += ntok * (record_bytes(self.d, b) + 1 + 2 * self.d)
+                    # the header: tier in the low four bits, empty slots in the high four
+                    hdr = int(self.page_bits[phys * self.hkv + g] if self.head_tiers else self.page_bits[phys])
+                    ntok = min(PAGE - (hdr >> 4), n - p * PAGE)
+                    tot += ntok * (record_bytes(self.d, hdr & 15) + 1 + 2 * self.d)
                 tot += self.hkv * (4 + 1 + (8 if self.page_off is not None else 0))
         tot += self.B * self.hq * self.d * 4 * 2
         return tot
@@ -335,3 +348,111 @@ def token_keys(w: Workload, s: int) -> slice:
     """Rows of ``keys``/``values``/``slot`` that belong to sequence s."""
     start = int(w.seq_lens[:s].astype(np.int64).sum())
     return slice(start, start + int(w.seq_lens[s]))
+
+
+# ---- the mixed-tier workload planned by the RDR controller ----------------
+#
+# Section 2.2 of the page: RDR chooses per state a residency and a tier under
+# a byte budget (distortion surrogate: the tier's angular error scaled by the
+# query and key magnitudes), keeps protected states (the sinks) at the widest
+# tier, and groups the retained states into tier-homogeneous pages.  This
+# workload takes the gqa_t32k keys, values and query and lets the controller
+# decide the tiers and the evictions that mixed_tiers draws at random.  The
+# plan itself is made by the library (ska_rdr_plan) or by the oracle; this
+# module only draws the controller's inputs and lays out a given plan.
+
+RDR_TIERS = (2, 4, 6, 8)
+# eps(b): RMS over random unit pairs at d = 128 of f_b(c_q, c_k) - <q, k>,
+# measured once with the CPU oracle (tests/golden/rdr_eps_d128.txt holds the
+# table and the script that wrote it)
+RDR_EPS = (2.710757e-01, 5.762753e-02, 1.450992e-02, 3.669538e-03)
+# sigma (the query magnitude and softmax scale folded into the surrogate) and
+# the budget (a fraction of keeping every state at the widest tier) are
+# chosen so that the plan evicts about half of the tokens and keeps the rest
+# at a spread of widths (about 26 / 54 / 16 / 4 % at b = 2 / 4 / 6 / 8), the
+# regime mixed_tiers draws at random
+RDR_SIGMA = 0.02
+RDR_BUDGET_FRAC = 0.42
+RDR_SINKS = 4             # protected first tokens
+
+
+@dataclasses.dataclass
+class RdrInputs:
+    base: Workload            # gqa_t32k-shaped keys, values, query (full pages)
+    utility: np.ndarray       # float32 [B][T]
+    key_norm: np.ndarray      # float32 [B][T]
+    protect: np.ndarray       # uint8 [B][T]
+    num_states: np.ndarray    # int32 [B]
+    budget: np.ndarray        # int64 [B]
+    tiers: tuple
+    eps: tuple
+    bytes_per_tier: tuple
+    sigma: float
+
+
+def rdr_inputs(scale: float = 1.0, batch: Optional[int] = None) -> RdrInputs:
+    """The controller's inputs for every token of a gqa_t32k-shaped batch:
+    a seeded utility per token (LogNormal(0, 1.5), five times larger over
+    the last 256 tokens, a recent window), its key norm (mean over KV heads),
+    the first RDR_SINKS tokens protected, and a byte budget of
+    RDR_BUDGET_FRAC of keeping every token at the widest tier."""
+    base = make("gqa_t32k", scale, batch=batch)
+    B, T = base.B, int(base.seq_lens.max())
+    r = np.random.default_rng(np.random.SeedSequence(SEED, spawn_key=(50,)))
+    util = r.lognormal(0.0, 1.5, size=(B, T)).astype(np.float32)
+    util[:, max(0, T - 256):] *= 5.0
+    kn = np.zeros((B, T), np.float32)
+    for s in range(B):
+        k = base.keys[token_keys(base, s)].astype(np.float64)
+        kn[s, : k.shape[0]] = np.sqrt((k * k).sum(axis=2)).mean(axis=1)
+    prot = np.zeros((B, T), np.uint8)
+    prot[:, :RDR_SINKS] = 1
+    per_state = tuple(base.hkv * (record_bytes(base.d, b) + 1 + 2 * base.d) for b in RDR_TIERS)
+    budget = (RDR_BUDGET_FRAC * base.seq_lens.astype(np.float64) * per_state[-1]).astype(np.int64)
+    return RdrInputs(base=base, utility=util, key_norm=kn, protect=prot, num_states=base.seq_lens.copy(),
+                     budget=budget, tiers=RDR_TIERS, eps=RDR_EPS, bytes_per_tier=per_state, sigma=RDR_SIGMA)
+
+
+def planned_workload(inp: RdrInputs, tier: np.ndarray, page: np.ndarray, slot: np.ndarray,
+                     page_hdr: np.ndarray, npages: np.ndarray) -> Workload:
+    """Lay out a plan: per sequence s, its npages[s] planned pages (headers
+    page_hdr[s], tier and empty slots) become physical pages of one shared,
+    shuffled pool, addressed through page_off (their sizes vary with the
+    tier), in plan order in row s of the block table; the retained tokens
+    (tier[s][i] > 0) go to slot slot[s][i] of planned page page[s][i].  The
+    row's length ends at its last page's last token."""
+    base = inp.base
+    B, hkv, d = base.B, base.hkv, base.d
+    npages = np.asarray(npages, np.int64)
+    total = int(npages.sum())
+    r = np.random.default_rng(np.random.SeedSequence(SEED, spawn_key=(51,)))
+    perm = r.permutation(total)
+    max_pages = max(1, int(npages.max()))
+    bt = np.zeros((B, max_pages), np.int32)
+    page_bits = np.zeros(total, np.uint8)
+    lens = np.zeros(B, np.int32)
+    keys, vals, slots = [], [], []
+    k0 = 0
+    for s in range(B):
+        n_p = int(npages[s])
+        phys = perm[k0: k0 + n_p]
+        k0 += n_p
+        bt[s, :n_p] = phys
+        page_bits[phys] = page_hdr[s][:n_p]
+        if n_p:
+            lens[s] = 16 * (n_p - 1) + PAGE - (int(page_hdr[s][n_p - 1]) >> 4)
+        n = int(inp.num_states[s])
+        kept = np.nonzero(tier[s][:n])[0]
+        rows = token_keys(base, s)
+        keys.append(base.keys[rows][kept])
+        vals.append(base.values[rows][kept])
+        slots.append(phys[page[s][kept]].astype(np.int64) * PAGE + slot[s][kept])
+    sizes = hkv * PAGE * np.array([record_bytes(d, int(b) & 15) for b in page_bits], np.uint64)
+    page_off = np.zeros(total, np.uint64)
+    if total:
+        page_off[1:] = np.cumsum(sizes)[:-1]
+    return Workload(name="mixed_tiers_rdr", d=d, hq=base.hq, hkv=hkv, B=B, radius_mode=base.radius_mode,
+                    tier_mask=sum(1 << b for b in inp.tiers), seq_lens=lens, block_table=bt, num_pages=total,
+                    page_bits=page_bits, page_off=page_off, bstride=max(inp.tiers),
+                    kcode_bytes=int(sizes.sum()), keys=np.concatenate(keys), values=np.concatenate(vals),
+                    slot=np.concatenate(slots), q=base.q)

@@ -91,9 +91,12 @@ def logit_bounds(w, rcode, rng, q=None, seq_lens=None):
         t = np.arange(n)
         phys = w.block_table[s, t // W.PAGE].astype(np.int64)
         for kv in range(w.hkv):
+            # resident: the slot below the page's count (header's high four bits: empty slots)
+            hdr = w.page_bits[phys * w.hkv + kv] if w.head_tiers else w.page_bits[phys]
+            res = (t % W.PAGE) < (W.PAGE - (hdr.astype(np.int64) >> 4))
             r = lev[kv][rcode[(phys * w.hkv + kv) * W.PAGE + t % W.PAGE]]
             for h in range(kv * g, (kv + 1) * g):
-                out[s, h, :n] = scale * qn[s, h] * r
+                out[s, h, t[res]] = scale * qn[s, h] * r[res]
     return out
 
 
@@ -155,3 +158,41 @@ def write_margins(path):
             f.write("| %s | %s | %.3g | %s | %s | %.2f | %s |\n" % (
                 t, lab, oe, "-" if le is None else "%.3g" % le, "-" if de is None else "%.3g" % de,
                 oe / OUT_TOL, "-" if le is None else "%.2f" % (le / LOGIT_TOL)))
+
+
+def planned_workloads(inp):
+    """The RDR controller on the GPU (ska_rdr_plan) and in the oracle on the
+    same inputs: the plans must agree bit for bit; each side's plan is laid
+    out on its own (workloads.planned_workload) and the layouts must agree.
+    Returns (workload from the GPU plan, workload from the oracle's plan)."""
+    import torch
+    from long_context_decode_ada_amd import ska
+    dev = "cuda"
+    B, T = inp.utility.shape
+    g = ska.rdr_plan(torch.from_numpy(inp.utility).to(dev), torch.from_numpy(inp.key_norm).to(dev),
+                     torch.from_numpy(inp.protect).to(dev), torch.from_numpy(inp.num_states).to(dev),
+                     torch.from_numpy(inp.budget).to(dev), inp.tiers, inp.eps, inp.bytes_per_tier, inp.sigma)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in g.items()}
+    o_tier = np.zeros((B, T), np.uint8)
+    o_page = np.full((B, T), -1, np.int32)
+    o_slot = np.full((B, T), -1, np.int32)
+    o_hdr, o_np = [], []
+    for s in range(B):
+        n = int(inp.num_states[s])
+        r = O.rdr_plan(inp.utility[s, :n], inp.key_norm[s, :n], inp.protect[s, :n], inp.tiers, inp.eps,
+                       inp.bytes_per_tier, int(inp.budget[s]), inp.sigma)
+        o_tier[s, :n], o_page[s, :n], o_slot[s, :n] = r["tier"], r["page"], r["slot"]
+        o_hdr.append(r["page_tier"])
+        o_np.append(len(r["page_tier"]))
+        assert g["status"][s] == r["status"] and g["lambda"][s] == r["lambda"], s
+        assert g["npages"][s] == len(r["page_tier"]), s
+        assert np.array_equal(g["page_tier"][s, : len(r["page_tier"])], r["page_tier"]), s
+        for k, v in (("tier", r["tier"]), ("page", r["page"]), ("slot", r["slot"])):
+            assert np.array_equal(g[k][s, :n], v), (s, k)
+    g_hdr = [g["page_tier"][s, : int(g["npages"][s])] for s in range(B)]
+    wg = W.planned_workload(inp, g["tier"], g["page"], g["slot"], g_hdr, g["npages"])
+    wo = W.planned_workload(inp, o_tier, o_page, o_slot, o_hdr, np.array(o_np))
+    for f in ("seq_lens", "block_table", "page_bits", "page_off", "slot", "keys", "values", "q"):
+        assert np.array_equal(getattr(wg, f), getattr(wo, f)), f
+    return wg, wo

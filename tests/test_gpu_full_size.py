@@ -12,11 +12,11 @@ import pytest
 
 from long_context_decode_ada_amd import workloads as W
 from oracle import oracle as O
-from tests.parity_util import compare, gpu_run, oracle_run, say
+from tests.parity_util import compare, gpu_run, oracle_run, planned_workloads, say
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["gqa_t32k", "long_t128k", "ragged_b64", "mixed_tiers"]
+FULL = ["gqa_t32k", "long_t128k", "ragged_b64", "mixed_tiers", "mixed_tiers_rdr"]
 
 
 @pytest.fixture(scope="module")
@@ -28,15 +28,19 @@ def full_runs():
             held.clear()            # keep one full-size workload in host memory at a time
             t0 = time.time()
             say("[full size] %s: generating" % name)
-            w = W.make(name)
+            if name == "mixed_tiers_rdr":
+                # tiers and evictions planned by the controller (GPU and oracle plans equal)
+                w, w_oracle = planned_workloads(W.rdr_inputs())
+            else:
+                w = w_oracle = W.make(name)
             say("[full size] %s: %d tokens, %d pages; GPU encode + decode (%.1fs)" %
                 (name, w.n_tokens, w.num_pages, time.time() - t0))
             g = gpu_run(w)
             say("[full size] %s: oracle calibrate + encode + decode (%.1fs)" % (name, time.time() - t0))
-            rng = O.calibrate(w.keys)
-            o = oracle_run(w, rng)
+            rng = O.calibrate(w_oracle.keys)
+            o = oracle_run(w_oracle, rng)
             say("[full size] %s: ready (%.1fs)" % (name, time.time() - t0))
-            held[name] = (w, g, o, rng)
+            held[name] = (w_oracle, g, o, rng)   # (the GPU plan's layout equals the oracle's)
         return held[name]
     return get
 

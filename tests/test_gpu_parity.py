@@ -241,3 +241,23 @@ def test_high_dynamic_range_keys(name, scale, batch):
     g16 = gpu_run(w)
     oe, _ = compare(w, g16, o, rng, label="%s, outlier channels, binary16 query direction" % name, out_tol=None)
     say("   binary16 direction: output error %.3g (bar 2e-3 not required here)" % oe)
+
+
+@pytest.mark.parametrize("name,scale,batch,splits", [("gqa_t32k", 1 / 32, 3, 0), ("gqa_t32k", 1 / 32, 3, 5),
+                                                     ("mixed_tiers", 1 / 16, 3, 0), ("tiny", 1.0, None, 0)])
+def test_partial_pages_inside_rows(name, scale, batch, splits):
+    """Page headers that count fewer than 16 tokens on pages anywhere in the
+    rows (the high four bits: empty slots at the page's end): the tokens in
+    those slots are still stored, so a decode that read them would differ;
+    single-tier pools run the tier-specialised kernel, mixed pools the
+    header-dispatched one."""
+    w = W.make(name, scale, batch=batch)
+    r = np.random.default_rng(77)
+    used = np.unique(np.concatenate([w.block_table[s, : (int(w.seq_lens[s]) + 15) // 16] for s in range(w.B)]))
+    pick = r.choice(used, size=max(1, len(used) // 3), replace=False)
+    w.page_bits[pick] = (w.page_bits[pick] & 15) | (r.integers(1, 16, size=len(pick)) << 4).astype(np.uint8)
+    g = gpu_run(w, num_splits=splits)
+    rng = O.calibrate(w.keys)
+    o = oracle_run(w, rng)
+    assert g["errors"] == 0
+    compare(w, g, o, rng, label="%s, partial pages inside rows, splits=%d" % (name, splits))

@@ -11,7 +11,7 @@ import pytest
 
 from long_context_decode_ada_amd import workloads as W
 from oracle import oracle as O
-from tests.parity_util import compare, gpu_run, oracle_run, say
+from tests.parity_util import compare, gpu_run, oracle_run, planned_workloads, say
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +100,13 @@ def _planned_workload(seed):
     return w, plans, keep_keys, keep_vals, rng
 
 
-def test_rdr_plan_drives_the_coded_decode():
+def test_rdr_planned_sequences_decode_as_one_row():
+    """An RDR-planned batch (utility = attention mass under the batch's
+    query, see _planned_workload) laid out as the controller packs it: each
+    sequence's tier pages, one partial page per tier, form ONE row of the
+    block table, the page headers carrying the tiers and the partial pages'
+    counts; the decode reads each sequence under one softmax and must match
+    the oracle on the same pages."""
     w, plans, keys_by_seq, vals_by_seq, rng = _planned_workload(22)
     T = max(p[0].shape[0] for p in plans)
     B = w.B
@@ -112,61 +118,37 @@ def test_rdr_plan_drives_the_coded_decode():
     for s, (ut, kt, pt, bt_) in enumerate(plans):
         n = ut.shape[0]
         u[s, :n], kn[s, :n], prot[s, :n], lens[s], budget[s] = ut, kt, pt, n, bt_
-    g = _gpu_plan(u, kn, prot, lens, budget, 0.05)
-    # pages of the plan -> physical pages of one shared pool
-    npg = g["npages"].astype(int)
-    total = int(npg.sum())
-    perm = rng.permutation(total)
-    max_pages = int(npg.max())
-    bt = np.zeros((B, max_pages), np.int32)
-    page_bits = np.zeros(total, np.uint8)
-    keys, vals, slots, kept_n = [], [], [], 0
-    k0 = 0
-    for s in range(B):
-        phys = perm[k0: k0 + npg[s]]
-        k0 += npg[s]
-        bt[s, : npg[s]] = phys
-        page_bits[phys] = g["page_tier"][s, : npg[s]]
-        n = int(lens[s])
-        kept = np.nonzero(g["tier"][s, :n])[0]
-        keys.append(keys_by_seq[s][kept])
-        vals.append(vals_by_seq[s][kept])
-        slots.append(phys[g["page"][s, kept]].astype(np.int64) * 16 + g["slot"][s, kept])
-        kept_n += len(kept)
-    # The decode maps token t of a row to slot t % 16 of page t / 16, so only
-    # a row's last page may be partly filled; the plan leaves one partial
-    # page per tier.  Each (sequence, tier) segment is therefore read as a
-    # row of its own (its pages in plan order, its tokens in slot order).
-    rows_bt, rows_len, rows_q = [], [], []
-    for s in range(B):
-        for t in TIERS:
-            pages = np.nonzero(g["page_tier"][s, : npg[s]] == t)[0]
-            if len(pages) == 0:
-                continue
-            n_t = int((g["tier"][s, : lens[s]] == t).sum())
-            row = np.zeros(max_pages, np.int32)
-            row[: len(pages)] = bt[s, pages]
-            rows_bt.append(row)
-            rows_len.append(n_t)
-            rows_q.append(w.q[s])
-    w2 = W.Workload(name="rdr", d=w.d, hq=w.hq, hkv=w.hkv, B=len(rows_bt), radius_mode=w.radius_mode,
-                    tier_mask=int(sum(1 << t for t in set(page_bits.tolist()))),
-                    seq_lens=np.array(rows_len, np.int32), block_table=np.stack(rows_bt), num_pages=total,
-                    page_bits=page_bits, page_off=None, bstride=8, kcode_bytes=0,
-                    keys=np.concatenate(keys), values=np.concatenate(vals), slot=np.concatenate(slots),
-                    q=np.stack(rows_q).astype(np.float32))
-    sizes = w2.hkv * 16 * np.array([O.kb(w2.d, int(b)) for b in page_bits], np.uint64)
-    w2.page_off = np.zeros(total, np.uint64)
-    w2.page_off[1:] = np.cumsum(sizes)[:-1]
-    w2.kcode_bytes = int(sizes.sum())
-    say("[rdr] %d sequences -> %d tier rows, %d pages, %d of %d tokens kept" %
-        (B, w2.B, total, kept_n, int(lens.sum())))
-    rng_r = O.calibrate(w2.keys)
-    gr = gpu_run(w2)
-    orr = oracle_run(w2, rng_r)
+    inp = W.RdrInputs(base=w, utility=u, key_norm=kn, protect=prot, num_states=lens, budget=budget,
+                      tiers=tuple(TIERS), eps=tuple(EPS), bytes_per_tier=tuple(BYTES), sigma=0.05)
+    wg, wo = planned_workloads(inp)
+    partial = [int((wo.page_bits[wo.block_table[s, : (wo.seq_lens[s] + 15) // 16]] >> 4 > 0).sum())
+               for s in range(B)]
+    say("[rdr] %d sequences, %d pages, %d of %d tokens kept, partial pages per row %s" %
+        (B, wo.num_pages, wo.n_tokens, int(lens.sum()), partial))
+    assert max(partial) >= 2                               # partial pages inside the rows
+    rng_r = O.calibrate(wo.keys)
+    gr = gpu_run(wg)
+    orr = oracle_run(wo, rng_r)
     for k in ("kcode", "rcode", "v"):
         assert np.array_equal(gr["pools"][k], orr["pools"][k]), k
-    compare(w2, gr, orr, rng_r, label="rdr pages")
+    assert gr["errors"] == 0
+    compare(wo, gr, orr, rng_r, label="rdr plan, one row per sequence")
+    gr4 = gpu_run(wg, num_splits=4, want_logits=False)
+    compare(wo, gr4, orr, rng_r, label="rdr plan, one row per sequence, 4 splits")
+
+
+def test_planned_mixed_tier_workload():
+    """The mixed-tier workload planned by the controller (workloads.rdr_inputs:
+    gqa_t32k keys, seeded utilities, sinks protected), at 1/16 of its length:
+    plans equal, then encode and decode at parity."""
+    inp = W.rdr_inputs(1 / 16)
+    wg, wo = planned_workloads(inp)
+    rng_r = O.calibrate(wo.keys)
+    gr = gpu_run(wg)
+    orr = oracle_run(wo, rng_r)
+    for k in ("kcode", "rcode", "v"):
+        assert np.array_equal(gr["pools"][k], orr["pools"][k]), k
+    compare(wo, gr, orr, rng_r, label="mixed_tiers_rdr 1/16")
 
 
 def test_many_sequences_after_a_small_call():

@@ -96,3 +96,55 @@ def test_outlier_channels():
     assert ra.max() / ra.min() > rp.max() / rp.min()
     with pytest.raises(ValueError):
         W.make("tiny", outliers=2)
+
+
+def test_rdr_parameters_match_the_measured_table():
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rdr_eps_d128.txt")
+    rows = {int(a): float(b) for a, b in (ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#"))}
+    assert W.RDR_EPS == tuple(rows[b] for b in W.RDR_TIERS)
+
+
+def oracle_plans(inp):
+    B, T = inp.utility.shape
+    tier = np.zeros((B, T), np.uint8)
+    page = np.full((B, T), -1, np.int32)
+    slot = np.full((B, T), -1, np.int32)
+    hdr, npg = [], []
+    for s in range(B):
+        n = int(inp.num_states[s])
+        r = O.rdr_plan(inp.utility[s, :n], inp.key_norm[s, :n], inp.protect[s, :n], inp.tiers, inp.eps,
+                       inp.bytes_per_tier, int(inp.budget[s]), inp.sigma)
+        tier[s, :n], page[s, :n], slot[s, :n] = r["tier"], r["page"], r["slot"]
+        hdr.append(r["page_tier"])
+        npg.append(len(r["page_tier"]))
+    return tier, page, slot, hdr, np.array(npg)
+
+
+def test_rdr_planned_workload_layout():
+    """The planned workload holds exactly the retained tokens, each at its
+    planned slot of a physical page whose header carries the plan's tier and
+    count; rows end at their last page's last token."""
+    inp = W.rdr_inputs(1 / 64)
+    tier, page, slot, hdr, npg = oracle_plans(inp)
+    w = W.planned_workload(inp, tier, page, slot, hdr, npg)
+    kept = int((tier > 0).sum())
+    assert w.keys.shape[0] == kept == len(w.slot) == w.n_tokens
+    assert len(np.unique(w.slot)) == kept
+    assert 0.3 < kept / tier.size < 0.7                   # about half evicted
+    assert w.num_pages == int(npg.sum())
+    for s in range(w.B):
+        n = int(inp.num_states[s])
+        rows = W.token_keys(inp.base, s)
+        idx = np.nonzero(tier[s, :n])[0]
+        start = int((tier[:s] > 0).sum())
+        assert np.array_equal(w.keys[start: start + len(idx)], inp.base.keys[rows][idx])
+        for j, i in enumerate(idx[:50]):
+            phys = int(w.slot[start + j]) // 16
+            assert phys == w.block_table[s, page[s, i]] and int(w.slot[start + j]) % 16 == slot[s, i]
+            assert w.page_bits[phys] & 15 == tier[s, i]
+            assert slot[s, i] < 16 - (w.page_bits[phys] >> 4)
+        last = int(w.block_table[s, npg[s] - 1])
+        assert w.seq_lens[s] == 16 * (npg[s] - 1) + 16 - (w.page_bits[last] >> 4)
+    # the sinks are kept at the widest tier
+    assert np.all(tier[:, : W.RDR_SINKS] == max(W.RDR_TIERS))
