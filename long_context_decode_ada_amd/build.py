@@ -66,6 +66,34 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     return LIB
 
 
+def build_abi_sanitized(verbose: bool = False) -> str:
+    """A program that drives the C ABI's host checks (tests/abi_sanitize_main.c)
+    linked with the host API built with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host code (device code unchanged) and
+    the kernel objects of build().  Returns the program's path."""
+    if not all(os.path.exists(os.path.join(BUILD, n + ".o")) for n, _, _ in UNITS):
+        build()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    obj = os.path.join(BUILD, "ska_api_sanitized.o")
+    flags = [f for n, src, f in UNITS if src == "ska_api.cpp"][0]
+    cmd = ["hipcc", "-x", "hip", *COMMON, *flags, *san, "-O1", "-g", "-c", os.path.join(CSRC, "ska_api.cpp"),
+           "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("compile failed: %s\n%s" % (" ".join(cmd), r.stderr))
+    exe = os.path.join(BUILD, "abi_sanitize")
+    objs = [os.path.join(BUILD, n + ".o") for n, src, _ in UNITS if src != "ska_api.cpp"]
+    cmd = ["hipcc", f"--offload-arch={ARCH}", *san, "-g", "-x", "c", os.path.join(ROOT, "tests", "abi_sanitize_main.c"),
+           "-x", "none", obj, *objs, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed: %s\n%s" % (" ".join(cmd), r.stderr))
+    if verbose:
+        print("built", exe)
+    return exe
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=0, help="parallel compiles (0: one per CPU, at most one per unit)")
