@@ -261,3 +261,16 @@ def test_partial_pages_inside_rows(name, scale, batch, splits):
     o = oracle_run(w, rng)
     assert g["errors"] == 0
     compare(w, g, o, rng, label="%s, partial pages inside rows, splits=%d" % (name, splits))
+
+
+def test_more_splits_than_the_weight_pass_holds():
+    """512 splits of one (sequence, KV head): more than the merge's LDS weight
+    pass holds (256), so the merge folds the partials element by element;
+    against the oracle and the automatic split layout."""
+    w = W.make("long_t128k", 1 / 2)                   # 4096 pages
+    rng = O.calibrate(w.keys)
+    o = oracle_run(w, rng, want_logits=False)
+    g = gpu_run(w, num_splits=512, want_logits=False)
+    compare(w, g, o, rng, label="512 splits")
+    g0 = gpu_run(w, want_logits=False)
+    assert np.abs(g["out"] - g0["out"]).max() < 1e-4
