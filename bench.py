@@ -116,7 +116,9 @@ def context_sweep(args, torch, ska, W):
     """ADA and dense-bf16 decode steps at T = 8K, 32K and 128K with gqa_t32k's
     batch shape (B=8, 32/8 heads, d=128, b=4, shuffled pages).  Keys and
     values are drawn N(0,1) on the GPU (the times do not depend on their
-    values); two pool copies alternate as in the main measurement."""
+    values); two pool copies alternate as in the main measurement, and each
+    path settles (about 45 ms of its steps) before its warm-up and timed
+    steps."""
     dev = "cuda"
     res = []
     for T in (8192, 32768, 131072):
@@ -143,7 +145,19 @@ def context_sweep(args, torch, ska, W):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
         def timed(fn, steps):
+            # settle as the main measurement does: about 45 ms of this path's
+            # steps back to back (the count from a short timing), then the
+            # warm-up and the timed steps
             for i in range(5):
+                fn(i)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(5):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            settle = int(math.ceil(45.0 / max(1e-3, e0.elapsed_time(e1) / 5)))
+            for i in range(settle + args.warmup):
                 fn(i)
             torch.cuda.synchronize()
             e0.record()
