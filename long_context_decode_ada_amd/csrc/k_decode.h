@@ -849,8 +849,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // ---- prologue.  Every global read it needs is issued at once: the
     // sequence length, the block-table entries of this wave's run (taken as
     // if the split were full, which it is except for the last split of a
-    // sequence) and the tables; the loads of the wave's first two pages then
-    // go out before the query preparation, which runs under their latency. ----
+    // sequence) and the tables; then the loads of the waves' first pages go
+    // out around the query preparation (see there), which runs under their
+    // latency. ----
     const int64_t bt_row = (int64_t)seq * A.max_pages;
     // block-table entries of a chunk: one clamped, unconditional load per lane
     auto bt_raw = [&](int c0) { return A.block_table[bt_row + min(c0 + lane, A.max_pages - 1)]; };
@@ -1084,18 +1085,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     if constexpr (TB != 0) {
         e_ph1 = ph1_raw;
 #pragma unroll
-        for (int i = 0; i < kBufs; ++i) {
-            dd[i] = rdesc(i, std::integral_constant<int, 0>{});
-            load_page<D, TB>(A, dd[i], kvh, R[i]);
-        }
+        for (int i = 0; i < kBufs; ++i) dd[i] = rdesc(i, std::integral_constant<int, 0>{});
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 
     if constexpr (APP) {
         // the wave whose run holds the new token's page stores the token
-        // first; with a single tier its first kBufs pages were requested
-        // above, so if the new page is among them they are requested again
+        // before it requests any page
         const int pnew = (len - 1) / kPage;
         if (pnew >= wp0 && pnew < wp1) {
             // the page's id: among this wave's staged block-table entries
@@ -1104,14 +1101,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             const int ph_new = rel < 64 ? __builtin_amdgcn_readlane(ph_raw, rel) : A.block_table[bt_row + pnew];
             append_token<D, TB>(A, seq, kvh, len_in, ph_new, akey, atau2, c2s, s2s, qT[wave],
                                 reinterpret_cast<uint8_t *>(mo[wave][0]));
-            if constexpr (TB != 0) {
-                if (pnew - wp0 < kBufs) {
-#pragma unroll
-                    for (int i = 0; i < kBufs; ++i) load_page<D, TB>(A, dd[i], kvh, R[i]);
-                }
-            }
         }
     }
+
+    // Single tier: the loads of the wave's first kBufs pages.  At the start
+    // of the kernel every wave of the chip requests its first pages at once
+    // and a wave's requests wait for room in the memory queue (about 2 us
+    // here); the waves that prepare a query row therefore request theirs
+    // after the preparation, which then runs while the other waves' loads
+    // wait and stream.
+    const bool prep_wave = TB != kDenseTB && (TB == 0 || wave < G);
+    auto first_loads = [&]() {
+        if constexpr (TB != 0) {
+#pragma unroll
+            for (int i = 0; i < kBufs; ++i) load_page<D, TB>(A, dd[i], kvh, R[i]);
+        }
+    };
+    if (!prep_wave) first_loads();
 
     // mixed tiers: the first chunk's headers and offsets are read now, so
     // their round trip runs under the query preparation
@@ -1131,7 +1137,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // plain search, so the codes always equal the defining ones.
     constexpr int kWpH = kWaves / G;   // waves per head
     static_assert(kWaves % G == 0, "heads divide the waves");
-    if (TB != kDenseTB && (TB == 0 || wave < G)) {
+    if (prep_wave) {
         const int h = wave % G, part = wave / G;
         constexpr int PL = D / 64;   // components per lane: a = lane * PL + r
         float xr[PL];
@@ -1253,6 +1259,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             }
             ++ti;
         }
+        first_loads();
     }
     __syncthreads();
     __builtin_amdgcn_s_setprio(0);

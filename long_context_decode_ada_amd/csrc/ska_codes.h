@@ -95,31 +95,40 @@ __device__ __forceinline__ int polar_guess(double xd, double Sd, int b) {
 __device__ __forceinline__ int polar_code_window(double x, double S, int b, const double *__restrict__ cos2,
                                                  const double *__restrict__ sin2, int g, double rel_err, bool &ok) {
 #pragma clang fp contract(off)
-    // straight-line (no branches): all four edges are read and decided with
-    // selects
+    // Straight-line: the eight table reads of the four edges go out together,
+    // then every decision is taken with bitwise operations on the compares
+    // (a branch per edge made each edge's reads wait for the previous edge).
     const int n = 1 << b;
     const double x2 = x * x;
     g = min(max(g, 0), n - 1);
+    int jc[4];
+    double c2[4], s2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        jc[i] = min(max(g - 1 + i, 1), n - 1);
+        c2[i] = cos2[jc[i]];
+        s2[i] = sin2[jc[i]];
+    }
+    const bool xle0 = x <= 0.0, xlt0 = x < 0.0, xge0 = x >= 0.0;
     int cnt = max(g - 2, 0);
     bool good = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = g - 1 + i;
-        const bool inr = j >= 1 && j <= n - 1;
-        const int jc = min(max(j, 1), n - 1);
-        const double a = cos2[jc] * S, c = sin2[jc] * x2;
-        const bool low = 2 * jc < n, mid = 2 * jc == n;
-        const bool prod = low ? (a >= c) : (a <= c);
-        const bool by_sign = mid || (low && x <= 0.0) || (!low && x >= 0.0);
-        const bool sure = by_sign || (fabs(a - c) > 2.0 * rel_err * a);
-        const bool p = mid ? (x <= 0.0) : (low ? (x <= 0.0 || prod) : (x < 0.0 && prod));
-        if (i < 3) cnt += (inr && p) ? 1 : 0;
-        good = good && (!inr || sure);
-        if (i == 0) good = good && (!inr || p);    // holds at g-1
-        if (i == 3) good = good && (!inr || !p);   // fails at g+2
+        const bool inr = (j >= 1) & (j <= n - 1);
+        const double a = c2[i] * S, c = s2[i] * x2;
+        const bool low = 2 * jc[i] < n, mid = 2 * jc[i] == n;
+        const bool prod = (low & (a >= c)) | (!low & (a <= c));
+        const bool by_sign = mid | (low & xle0) | (!low & xge0);
+        const bool sure = by_sign | (fabs(a - c) > 2.0 * rel_err * a);
+        const bool p = (mid & xle0) | (!mid & low & (xle0 | prod)) | (!mid & !low & xlt0 & prod);
+        if (i < 3) cnt += (int)(inr & p);
+        good = good & (!inr | sure);
+        if (i == 0) good = good & (!inr | p);    // holds at g-1
+        if (i == 3) good = good & (!inr | !p);   // fails at g+2
     }
-    const bool zero = (x == 0.0 && S == 0.0);
-    ok = zero || good;
+    const bool zero = (x == 0.0) & (S == 0.0);
+    ok = zero | good;
     return zero ? 0 : cnt;
 }
 
