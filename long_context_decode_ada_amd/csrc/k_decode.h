@@ -1036,8 +1036,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     };
     // kBufs register sets: the loads of pages k+1 .. k+kBufs-1 are in flight
     // while page k is computed.  Loads are issued unconditionally (past the
-    // end they repeat the last page) so that the wait before each compute
-    // only covers the loads of the page being computed.
+    // end through empty descriptors that read nothing) so that the wait
+    // before each compute only covers the loads of the page being computed.
     PageBuf<D> R[kBufs];
     PageDesc dd[kBufs];
     auto issue_chunk = [&]() {
@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
         for (int i = 0; i < kBufs; ++i) {
             dd[i] = desc(max(0, min(i, nvalid - 1)));
-            dd[i].live = nvalid > 0;
+            dd[i].live = i < nvalid;
             load_page<D, TB>(A, dd[i], kvh, R[i]);
         }
     };
@@ -1104,39 +1104,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         }
     }
 
-    // Single tier: the loads of the wave's first kBufs pages.  At the start
-    // of the kernel every wave of the chip requests its first pages at once
-    // and a wave's requests wait for room in the memory queue (about 2 us
-    // here); the waves that prepare a query row therefore request theirs
-    // after the preparation, which then runs while the other waves' loads
-    // wait and stream.
-    const bool prep_wave = TB != kDenseTB && (TB == 0 || wave < G);
+    // The loads of the wave's first pages.  At the start of the kernel every
+    // wave of the chip requests its first pages at once, and a wave's requests
+    // wait for room in the memory queue (about 2 us here).  The waves that
+    // prepare a query row therefore request theirs after the preparation,
+    // which then runs while the other waves' loads wait and stream.  (With
+    // mixed tiers every wave's first chunk is listed and requested in the
+    // page loop, after the preparation.)
+    // (mixed tiers: the kWaves/G waves of a head share its tiers, each taking
+    // every (kWaves/G)-th tier present; a wave left without one loads early)
+    constexpr int kWpH = kWaves / G;   // waves per head
+    static_assert(kWaves % G == 0, "heads divide the waves");
+    const int ntiers = TB != 0 ? 1 : __builtin_popcount(A.tier_mask & 0x1FCu);
+    const bool prep_wave = TB != kDenseTB && (TB == 0 ? wave / G < ntiers : wave < G);
     auto first_loads = [&]() {
         if constexpr (TB != 0) {
 #pragma unroll
             for (int i = 0; i < kBufs; ++i) load_page<D, TB>(A, dd[i], kvh, R[i]);
         }
     };
-    if (!prep_wave) first_loads();
-
-    // mixed tiers: the first chunk's headers and offsets are read now, so
-    // their round trip runs under the query preparation
-    if constexpr (TB == 0) {
-        if (wp0 < wp1) page_list(wp0, ph_first);
-    }
 
     // Query prep, section 2.1's c_q: per tier, the angle codes of each query
     // row and the decoded direction u_a = (prod_{k<a} sin c_k) * cos c_a
-    // (D/64 components per lane).  One wave per head and tier: with a
-    // single tier waves 0..G-1, with mixed tiers all kWaves/G waves of a head,
-    // each taking every (kWaves/G)-th tier.  The suffix sums of squares the
-    // codes compare against are taken by a wave scan (fast, but in another
-    // order than the keys' backward sum); a code is accepted only when its
-    // decisions hold with a margin covering that reordering.  Any decision
-    // inside the margin sends the wave to the exact backward sum and the
-    // plain search, so the codes always equal the defining ones.
-    constexpr int kWpH = kWaves / G;   // waves per head
-    static_assert(kWaves % G == 0, "heads divide the waves");
+    // (D/64 components per lane): with a single tier one wave per head
+    // (waves 0..G-1), with mixed tiers the head's waves share its tiers.  The
+    // suffix sums of squares the codes compare against are taken by a wave
+    // scan (fast, but in another order than the keys' backward sum); a code
+    // is accepted only when its decisions hold with a margin covering that
+    // reordering.  Any decision inside the margin sends the wave to the exact
+    // backward sum and the plain search, so the codes always equal the
+    // defining ones.  The bins of every tier are uniform and nest: each edge
+    // j*pi/2^b is the edge (j*2^(m-b))*pi/2^m of the widest tier m, with the
+    // same binary64 table values, so a code at b is the code at m shifted
+    // right by m - b (the azimuth's half-plane offset shifts with it).  The
+    // codes are decided once, at the widest tier present.
     if (prep_wave) {
         const int h = wave % G, part = wave / G;
         constexpr int PL = D / 64;   // components per lane: a = lane * PL + r
@@ -1164,9 +1165,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         float ux[PL];
 #pragma unroll
         for (int r = 0; r < PL; ++r) ux[r] = 0.f;
-        if (__builtin_expect(A.query_mode == 1, 0)) {
+        const bool exact_q = A.query_mode == 1;
+        if (__builtin_expect(exact_q, 0)) {
 #pragma unroll
             for (int r = 0; r < PL; ++r) ux[r] = qn > 0.0 ? (float)((double)xr[r] / qn) : 0.f;
+        }
+        // the codes at the widest tier present (polar; for the azimuth the
+        // code within its half plane)
+        const int bm = TB != 0 ? TB : 31 - __builtin_clz(A.tier_mask & 0x1FCu);
+        int code_m[PL];
+#pragma unroll
+        for (int r = 0; r < PL; ++r) code_m[r] = 0;
+        if (!exact_q) {
+            bool ok = true;
+#pragma unroll
+            for (int r = 0; r < PL; ++r) {
+                const int a = lane * PL + r;
+                const bool az = a == D - 2;
+                const double x = az ? xpa : (double)xr[r];
+                const double S = az ? ypa * ypa : Sr[r];
+                const int bb = az ? bm - 1 : bm;
+                bool okr;
+                code_m[r] = polar_code_window(x, S, bb, c2s + thr_off(bb), s2s + thr_off(bb), polar_guess(x, S, bb),
+                                              az ? 0.0 : 5e-14, okr);
+                ok = ok && (a >= D - 1 || okr);
+            }
+            if (__builtin_amdgcn_ballot_w64(!ok) != 0) {
+                // rare: the exact backward suffix sums (one lane), then the plain search
+                if (lane == 0) {
+                    double T = 0.0;
+                    for (int a2 = D - 1; a2 >= 0; --a2) {
+                        qT[wave][a2] = T;   // sum over k > a2
+                        T = add_square(T, qs[h][a2]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < PL; ++r) {
+                    const int a = lane * PL + r;
+                    if (a < D - 2) {
+                        const double x = (double)xr[r], S = qT[wave][a];
+                        code_m[r] = polar_code_near(x, S, bm, c2s + thr_off(bm), s2s + thr_off(bm), code_m[r]);
+                    } else if (a == D - 2) {
+                        code_m[r] = polar_code_near(xpa, ypa * ypa, bm - 1, c2s + thr_off(bm - 1), s2s + thr_off(bm - 1),
+                                                    code_m[r]);
+                    }
+                }
+            }
         }
         int ti = 0;
         // the tiers present: only the kernel's own when the pool has one
@@ -1177,56 +1221,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                 continue;
             }
             float uv[PL];
-            if (A.query_mode == 1) {
+            if (exact_q) {
 #pragma unroll
                 for (int r = 0; r < PL; ++r) uv[r] = ux[r];
             } else {
-                // one code per component; polar and azimuth share the code path
-                int code[PL];
-                bool ok = true;
-#pragma unroll
-                for (int r = 0; r < PL; ++r) {
-                    const int a = lane * PL + r;
-                    const bool az = a == D - 2;
-                    const double x = az ? xpa : (double)xr[r];
-                    const double S = az ? ypa * ypa : Sr[r];
-                    const int bb = az ? b - 1 : b;
-                    bool okr;
-                    const int g = polar_code_window(x, S, bb, c2s + thr_off(bb), s2s + thr_off(bb),
-                                                    polar_guess(x, S, bb), az ? 0.0 : 5e-14, okr);
-                    code[r] = g;
-                    ok = ok && (a >= D - 1 || okr);
-                }
-                if (__builtin_amdgcn_ballot_w64(!ok) != 0) {
-                    // rare: the exact backward suffix sums (one lane), then the plain search
-                    if (lane == 0) {
-                        double T = 0.0;
-                        for (int a2 = D - 1; a2 >= 0; --a2) {
-                            qT[wave][a2] = T;   // sum over k > a2
-                            T = add_square(T, qs[h][a2]);
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < PL; ++r) {
-                        const int a = lane * PL + r;
-                        if (a < D - 2) {
-                            const double x = (double)xr[r], S = qT[wave][a];
-                            code[r] = polar_code_near(x, S, b, c2s + thr_off(b), s2s + thr_off(b), code[r]);
-                        } else if (a == D - 2) {
-                            code[r] = polar_code_near(xpa, ypa * ypa, b - 1, c2s + thr_off(b - 1), s2s + thr_off(b - 1),
-                                                      code[r]);
-                        }
-                    }
-                }
                 float cs[PL], sn[PL];
 #pragma unroll
                 for (int r = 0; r < PL; ++r) {
                     const int a = lane * PL + r;
+                    const int code = code_m[r] >> (bm - b);
                     cs[r] = 1.f;
                     sn[r] = 1.f;
                     if (a < D - 1) {
-                        const int e = (a == D - 2) ? lut_azimuth(b) + (hp ? (1 << (b - 1)) : 0) + code[r]
-                                                   : lut_polar(b) + code[r];
+                        const int e = (a == D - 2) ? lut_azimuth(b) + (hp ? (1 << (b - 1)) : 0) + code
+                                                   : lut_polar(b) + code;
                         const float2 v = lut[e];
                         cs[r] = v.x;
                         sn[r] = v.y;
@@ -1259,6 +1267,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             }
             ++ti;
         }
+        first_loads();
+    } else {
         first_loads();
     }
     __syncthreads();
@@ -1359,8 +1369,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     int ph_next = -1;   // the next chunk's block-table entries, requested a chunk ahead
     for (int c0 = wp0; TB == 0 && c0 < wp1; c0 += 64) {
-        if (c0 != wp0) start_chunk(c0, ph_next);
-        else issue_chunk();   // (its page list was built before the query preparation)
+        start_chunk(c0, c0 == wp0 ? ph_first : ph_next);
         ph_next = bt_raw(c0 + 64);
         ph_next = (c0 + 64 + lane < wp1) ? ph_next : -1;   // (all -1 past the wave's run)
         if (nvalid == 0) continue;
@@ -1373,6 +1382,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                     compute_page<D, G, TB, DBG, QF>(A, dd[i], R[i], len, head0, u, qd, sq, lut, rlev, pb, st, acc);
                 }
                 dd[i] = desc(min(k + i + kBufs, last));
+                dd[i].live = k + i + kBufs < nvalid;   // (past the chunk: empty descriptors, no reads)
                 load_page<D, TB>(A, dd[i], kvh, R[i]);
                 __builtin_amdgcn_sched_barrier(0);
             }
