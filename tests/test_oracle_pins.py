@@ -74,6 +74,34 @@ def test_exact_edges_and_zero_vectors(b):
     assert all(c2 >= c1 for c1, c2 in zip(codes, codes[1:]))
 
 
+@pytest.mark.parametrize("b", [2, 3, 4, 6])
+def test_codes_nest_across_tiers(b):
+    """The bins of every width are uniform over the same range, so each edge
+    j*pi/2^b of a narrow tier is the edge (j*2^(8-b))*pi/2^8 of the 8-bit
+    tier: the narrow code is the 8-bit code shifted right by 8 - b (the
+    azimuth's half-plane offset shifts with it).  Checked on the edge tables
+    (identical binary64 values), on random angles, and on inputs placed on
+    8-bit edges, where the exact predicates decide."""
+    k = 8 - b
+    c2b, s2b = O.angle_thresholds(b)
+    c28, s28 = O.angle_thresholds(8)
+    j = np.arange(1, 1 << b)
+    assert np.array_equal(c2b[j], c28[j << k]) and np.array_equal(s2b[j], s28[j << k])
+    rng = np.random.default_rng(3000 + b)
+    n = 3000
+    x = rng.standard_normal(n) * rng.choice([1e-3, 1.0, 1e3], n)
+    y = rng.standard_normal(n) * rng.choice([1e-3, 1.0, 1e3], n)
+    # on (or within rounding of) 8-bit edges: cos and sin of j*pi/256
+    je = rng.integers(1, 256, 400)
+    xe = np.cos(je * PI / 256)
+    ye = np.sin(je * PI / 256)
+    for xi, yi in zip(np.r_[x, xe], np.r_[y, ye]):
+        S = yi * yi
+        assert O.polar_code(xi, S, b) == O.polar_code(xi, S, 8) >> k
+        assert O.azimuth_code(xi, yi, b) == O.azimuth_code(xi, yi, 8) >> k
+        assert O.azimuth_code(xi, -yi, b) == O.azimuth_code(xi, -yi, 8) >> k
+
+
 def test_thresholds_are_squared_cos_sin_of_edges():
     for b in (2, 4, 8):
         c2, s2 = O.angle_thresholds(b)
