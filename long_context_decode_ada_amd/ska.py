@@ -260,6 +260,34 @@ def decode_attention(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, s
     return out
 
 
+def prepared_decode(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                    out: torch.Tensor, scale: float = 0.0, num_splits: int = 0, stream=None,
+                    k_dense: Optional[torch.Tensor] = None):
+    """decode_attention (or, given k_dense, dense_decode_attention) with its
+    arguments checked and marshalled once: returns a callable that enqueues
+    the same call each time it is called, for a decode loop over fixed
+    buffers (it holds references to the tensors)."""
+    B, hq, d = q.shape
+    _decode_checks(cache, q, block_table, seq_lens, out, None)
+    tail = (B, hq, _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), float(scale), int(num_splits),
+            _ptr(out), None, _stream(stream))
+    if k_dense is None:
+        name, fn, args = "ska_decode_attention", lib().ska_decode_attention, (cache.handle, _ptr(q)) + tail
+    else:
+        P = cache.pools
+        _dev("k_dense", k_dense, _BF16_BITS, (P.num_pages, P.hkv, PAGE, P.d))
+        name, fn = "ska_dense_decode_attention", lib().ska_dense_decode_attention
+        args = (cache.handle, _ptr(k_dense), _ptr(q)) + tail
+    keep = (cache, q, block_table, seq_lens, out, k_dense)
+
+    def call():
+        s = fn(*args)
+        if s != SKA_OK:
+            raise SkaError(s, name)
+        return keep[4]
+    return call
+
+
 def decode_attention_noalloc(cache: Cache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                              scale: float = 0.0, num_splits: int = 0, out: Optional[torch.Tensor] = None,
                              stream=None) -> torch.Tensor:

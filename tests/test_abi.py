@@ -188,3 +188,40 @@ def test_decode_outside_the_reserved_maxima_is_rejected():
     assert bool(torch.isfinite(out[:2]).all()) and bool((out[2] == 7.0).all())
     assert ska.device_errors(cache) == 0
     cache.free()
+
+
+@pytest.mark.gpu
+def test_prepared_decode_call_matches_the_plain_call():
+    """The prepared call (arguments checked and marshalled once) enqueues the
+    same library call: identical outputs, coded and dense, on every call."""
+    import numpy as np
+    import torch
+    from long_context_decode_ada_amd import workloads as W
+    w = W.make("gqa_t32k", 1 / 64, batch=2)
+    dev = "cuda"
+    cache = ska.Cache(ska.DevicePools.for_workload(w, device=dev))
+    ska.encode_keys(cache, torch.from_numpy(w.keys).to(dev), torch.from_numpy(w.values.view(np.int16)).to(dev),
+                    torch.from_numpy(w.slot).to(dev))
+    q = torch.from_numpy(w.q).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    kd = torch.zeros((w.num_pages, w.hkv, 16, w.d), dtype=torch.int16, device=dev)
+    ska.decompress_keys(cache, bt, sl, kd)
+    ref = ska.decode_attention(cache, q, bt, sl, num_splits=3)
+    ref_d = ska.dense_decode_attention(cache, kd, q, bt, sl, num_splits=3)
+    out = torch.full_like(ref, 7.0)
+    call = ska.prepared_decode(cache, q, bt, sl, out, num_splits=3)
+    dcall = ska.prepared_decode(cache, q, bt, sl, out, num_splits=3, k_dense=kd)
+    for _ in range(3):
+        out.fill_(7.0)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        out.fill_(7.0)
+        dcall()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_d)
+    with pytest.raises(ValueError):                        # checked once, at preparation
+        ska.prepared_decode(cache, q, bt, sl, out[:1])
+    assert ska.device_errors(cache) == 0
+    cache.free()
