@@ -1449,6 +1449,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __syncthreads();
     if (!s_last) return;
     auto ld = [](float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    // Up to kMergeFast splits: each thread requests, at once, its element's
+    // partial of every split and its head's (m, l) pairs (one 8-byte load
+    // each), then forms the weights itself: one round trip, no barrier.  The
+    // merge runs while the rest of the chip still streams pages, so each
+    // round trip is long.  The loads are unconditional: N, the split count
+    // rounded up to a power of two (at least 4), are issued, with indices
+    // past the last split clamped to it.  (Fewer in the mixed-tier kernel,
+    // whose register file is full.)
+    constexpr int kMergeFast = TB == 0 ? 8 : 32;
+    auto merge_fast = [&](auto n_c) {
+        constexpr int N = decltype(n_c)::value;
+        for (int idx = tid; idx < G * D; idx += kThreads) {
+            const int h = idx / D, e = idx % D;
+            const int64_t row = head0 + h;
+            float *po = A.part_o + row * A.nsplit * D + e;
+            const uint64_t *pml = reinterpret_cast<const uint64_t *>(A.part_ml + row * A.nsplit * 2);
+            float pv[N];
+            uint64_t mlv[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int sc = min(i, ns_g - 1);
+                pv[i] = ld(po + (int64_t)sc * D);
+                mlv[i] = __hip_atomic_load(pml + sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            float M = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if (i < ns_g) M = fmaxf(M, __uint_as_float((uint32_t)mlv[i]));
+            float L = 0.f, O = 0.f;
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    const float m = __uint_as_float((uint32_t)mlv[i]);
+                    const float w = (i < ns_g && m != -INFINITY) ? exp2f(m - M) : 0.f;
+                    L += w * __uint_as_float((uint32_t)(mlv[i] >> 32));
+                    O += w * pv[i];
+                }
+            }
+            A.out[row * D + e] = L > 0.f ? O / L : 0.f;
+        }
+        if (tid == 0) __hip_atomic_store(&A.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (ns_g <= 4) return merge_fast(std::integral_constant<int, 4>{});
+    if (ns_g <= 8) return merge_fast(std::integral_constant<int, 8>{});
+    if (kMergeFast >= 16 && ns_g <= 16) return merge_fast(std::integral_constant<int, (kMergeFast >= 16 ? 16 : 8)>{});
+    if (kMergeFast >= 32 && ns_g <= 32) return merge_fast(std::integral_constant<int, (kMergeFast >= 32 ? 32 : 8)>{});
     constexpr int kMergeMax = 256;   // splits whose weights one LDS pass holds
     if (ns_g <= kMergeMax) {
         // Each split's weight, once per head (one wave per head, in the LDS
