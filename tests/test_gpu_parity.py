@@ -78,6 +78,30 @@ def test_split_count_and_determinism():
             assert np.abs(g["out"] - base["out"]).max() < 1e-4
 
 
+@pytest.mark.parametrize("name,scale,counts", [
+    # 128 pages per row: explicit counts giving 4, 5, 8, 9, 16, 19, 32 and 43
+    # non-empty splits, on both sides of each size of the one-round merge
+    # (4, 8, 16, 32 loads per thread) and past it (the LDS weight pass)
+    ("gqa_t32k", 1 / 16, (4, 5, 8, 9, 16, 19, 32, 43)),
+    # the mixed-tier kernel merges up to 8 splits in one round
+    ("mixed_tiers", 1 / 8, (5, 8, 9, 12)),
+])
+def test_merge_paths_at_their_split_count_boundaries(name, scale, counts):
+    w = W.make(name, scale, batch=2)
+    rng = O.calibrate(w.keys)
+    o = oracle_run(w, rng)
+    base = None
+    for ns in counts:
+        g = gpu_run(w, num_splits=ns, repeat=2)
+        assert np.array_equal(g["outs"][0], g["outs"][1]), "run-to-run difference at %d splits" % ns
+        compare(w, g, o, rng, label="%s splits=%d" % (name, ns))
+        if base is None:
+            base = g
+        else:
+            assert np.array_equal(g["logits"], base["logits"], equal_nan=True)
+            assert np.abs(g["out"] - base["out"]).max() < 1e-4
+
+
 def test_ragged_edges_zero_one_and_page_boundaries():
     w = W.make("gqa_t32k", 1 / 32, batch=8)          # 1024 tokens encoded per sequence
     lens = np.array([0, 1, 15, 16, 17, 31, 33, 1024], np.int32)
