@@ -1449,15 +1449,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __syncthreads();
     if (!s_last) return;
     auto ld = [](float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    // Up to kMergeFast splits: each thread requests, at once, its element's
-    // partial of every split and its head's (m, l) pairs (one 8-byte load
-    // each), then forms the weights itself: one round trip, no barrier.  The
-    // merge runs while the rest of the chip still streams pages, so each
-    // round trip is long.  The loads are unconditional: N, the split count
-    // rounded up to a power of two (at least 4), are issued, with indices
-    // past the last split clamped to it.  (Fewer in the mixed-tier kernel,
-    // whose register file is full.)
+    // Up to kMergeFast splits: one round of loads and no barrier.  A wave's
+    // 64 elements belong to one head (D is a multiple of 64): lane i requests
+    // split i's (m, l) pair (one 8-byte load) while every lane requests its
+    // element's partial of each split; the wave reduces the maxima and the
+    // weighted sums across lanes and reads each split's weight from its lane.
+    // The merge runs while the rest of the chip still streams pages, so each
+    // round trip is long.  The partial loads are unconditional: N, the split
+    // count rounded up to a power of two (at least 4), are issued, with
+    // indices past the last split clamped to it.  (Fewer in the mixed-tier
+    // kernel, whose register file is full.)
     constexpr int kMergeFast = TB == 0 ? 8 : 32;
+    static_assert(D % 64 == 0, "a wave's merge elements share one head");
     auto merge_fast = [&](auto n_c) {
         constexpr int N = decltype(n_c)::value;
         for (int idx = tid; idx < G * D; idx += kThreads) {
@@ -1465,29 +1468,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             const int64_t row = head0 + h;
             float *po = A.part_o + row * A.nsplit * D + e;
             const uint64_t *pml = reinterpret_cast<const uint64_t *>(A.part_ml + row * A.nsplit * 2);
+            const bool has = lane < ns_g;
+            const uint64_t mlv = __hip_atomic_load(pml + min(lane, ns_g - 1), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
             float pv[N];
-            uint64_t mlv[N];
 #pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int sc = min(i, ns_g - 1);
-                pv[i] = ld(po + (int64_t)sc * D);
-                mlv[i] = __hip_atomic_load(pml + sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            float M = -INFINITY;
+            for (int i = 0; i < N; ++i) pv[i] = ld(po + (int64_t)min(i, ns_g - 1) * D);
+            const float m = has ? __uint_as_float((uint32_t)mlv) : -INFINITY;
+            float M = m;
 #pragma unroll
-            for (int i = 0; i < N; ++i)
-                if (i < ns_g) M = fmaxf(M, __uint_as_float((uint32_t)mlv[i]));
-            float L = 0.f, O = 0.f;
-            if (M != -INFINITY) {
+            for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+            const float w = (m != -INFINITY) ? exp2f(m - M) : 0.f;
+            float L = has ? w * __uint_as_float((uint32_t)(mlv >> 32)) : 0.f;
 #pragma unroll
-                for (int i = 0; i < N; ++i) {
-                    const float m = __uint_as_float((uint32_t)mlv[i]);
-                    const float w = (i < ns_g && m != -INFINITY) ? exp2f(m - M) : 0.f;
-                    L += w * __uint_as_float((uint32_t)(mlv[i] >> 32));
-                    O += w * pv[i];
-                }
-            }
-            A.out[row * D + e] = L > 0.f ? O / L : 0.f;
+            for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+            float O = 0.f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) O += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i)) * pv[i];
+            A.out[row * D + e] = (M != -INFINITY && L > 0.f) ? O / L : 0.f;
         }
         if (tid == 0) __hip_atomic_store(&A.counters[group], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
