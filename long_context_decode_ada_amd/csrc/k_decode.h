@@ -1395,13 +1395,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         mml[wave][lane][0] = st.m;
         mml[wave][lane][1] = lsum;
     }
+    // rows 0..2G-1 of the accumulators (P hi and lo): lanes of the first
+    // 2G/4 lane groups hold them (all four of a group's rows when 2G is a
+    // multiple of 4), so one condition covers every store
+    if (4 * q4 < 2 * G) {
 #pragma unroll
-    for (int k = 0; k < NT; ++k) {
-        const float a4[4] = {acc[k].x, acc[k].y, acc[k].z, acc[k].w};
+        for (int k = 0; k < NT; ++k) {
+            const float a4[4] = {acc[k].x, acc[k].y, acc[k].z, acc[k].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 4 * q4 + i;
-            if (rr < 2 * G) mo[wave][rr][16 * k + n16] = a4[i];
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 4 * q4 + i;
+                if ((2 * G) % 4 == 0 || rr < 2 * G) mo[wave][rr][16 * k + n16] = a4[i];
+            }
         }
     }
     __syncthreads();
