@@ -188,13 +188,13 @@ ska_status ska_decode_attention(const ska_cache *cache, const float *q, int batc
 /* ska_decode_attention_noalloc -- for callers that cannot allocate device
  * memory (code under graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): ska_decode_attention (without logits_dbg) with its split
- * partials and merge counters in a static device array of the library
+ * partials, merge counters and unit order in a static device array of the library
  * (16 MiB per GPU, kept until the process ends) instead of the cache's
  * workspace.  Allocates nothing and frees nothing; the first call on a GPU
  * looks the array up and clears its counters with a small kernel on
  * `stream`.  Rejects with SKA_ERR_INVALID, before enqueueing anything, a
  * call whose partials (batch * num_q_heads * splits rows of (d + 2) floats)
- * exceed 16 MiB - 256 KiB or whose batch * Hkv exceeds 65536, and anything
+ * exceed 16 MiB - 384 KiB or whose batch * Hkv exceeds 65536, and anything
  * ska_decode_attention rejects.  Every call on one GPU shares that GPU's
  * array: calls that overlap on the device (different streams, not ordered
  * by the caller) race and give wrong results.  Results equal

@@ -782,43 +782,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const int tid = threadIdx.x, lane = tid & 63;
     int len_known = 0;
     if (A.compact) {
-        // Compacted grid: every wave reads the batch's lengths and this
-        // workgroup takes the slot-th unit with pages of its KV head, the
-        // highest split index first (in dispatch order), so the slots past
-        // the last unit, which exit at once, come at the end.  A sequence
-        // with no page still has one unit (it writes its zero rows).
-        constexpr int kC = kCompactMaxBatch / 64;
-        int ns[kC], ln[kC];
-#pragma unroll
-        for (int c = 0; c < kC; ++c) {
-            const int s = c * 64 + lane;
-            ln[c] = s < (int)gridDim.y ? A.seq_lens[s] : 0;
-        }
-#pragma unroll
-        for (int c = 0; c < kC; ++c) {
-            const int np = (max(0, min(ln[c], A.max_pages * kPage)) + kPage - 1) / kPage;
-            ns[c] = c * 64 + lane < (int)gridDim.y ? max(1, splits_of(A, np)) : 0;
-        }
-        int slot = (int)(blockIdx.z * gridDim.y + blockIdx.y);
-        seq = -1;
-        for (int j = A.nsplit - 1; j >= 0 && seq < 0; --j) {
-#pragma unroll
-            for (int c = 0; c < kC; ++c) {
-                const uint64_t m = __builtin_amdgcn_ballot_w64(ns[c] > j);
-                const int n = __popcll(m);
-                if (seq < 0 && slot < n) {
-                    // the slot-th set bit of m
-                    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    const uint64_t hit = __builtin_amdgcn_ballot_w64(((m >> lane) & 1) && below == slot);
-                    const int l = __builtin_ffsll((long long)hit) - 1;
-                    seq = c * 64 + l;
-                    split = j;
-                    len_known = __builtin_amdgcn_readlane(ln[c], l);
-                }
-                if (seq < 0) slot -= n;
-            }
-        }
-        if (seq < 0) return;   // a slot past the last unit
+        // Compacted grid: this workgroup's unit, in decreasing size (written
+        // by k_unit_order), and its sequence's length.  A sequence with no
+        // page still has one unit (it writes its zero rows).
+        const int2 ent = A.unit_table[blockIdx.z * gridDim.y + blockIdx.y];
+        if (ent.x < 0) return;   // a slot past the last unit
+        seq = ent.x >> 16;
+        split = ent.x & 0xFFFF;
+        len_known = ent.y;
     }
     seq = __builtin_amdgcn_readfirstlane(seq);
     split = __builtin_amdgcn_readfirstlane(split);

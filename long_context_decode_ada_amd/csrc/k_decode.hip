@@ -270,8 +270,87 @@ hipError_t launch_decompress(const DecodeArgs &a, int d, int B, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The order of the units of a batch that runs in several rounds.  The
+// workgroup dispatcher starts workgroups strictly in grid order, and on each
+// XCD a workgroup waits for a free CU in its own shader engine (consecutive
+// slots of an XCD cycle over its engines) while the later ones wait behind
+// it; units of very different sizes in consecutive slots therefore left up to
+// a quarter of the CUs idle (in-kernel timestamps on a ragged batch of 64).
+// Handed out in decreasing size, neighbouring slots hold units of similar
+// size and the engines fill and drain together.  One workgroup: the units of
+// each sequence (as the decode splits it) get the key (size descending, split
+// descending, sequence), unique, so the order is the same on every call; a
+// bitonic sort in LDS; then slot i of the table receives the i-th unit and
+// its sequence's length (-1 past the last unit).  Which workgroup computes a
+// unit does not change the unit's result, so the outputs do not depend on
+// the order.
+constexpr int kUnitSortThreads = 1024;
+static_assert(kCompactMaxBatch <= kUnitSortThreads, "one thread per sequence");
+__global__ __launch_bounds__(kUnitSortThreads) void k_unit_order(DecodeArgs A, int B, int nslots) {
+    __shared__ uint64_t key[kUnitSortMax];
+    __shared__ int scan[kUnitSortThreads];
+    __shared__ int lens[kCompactMaxBatch];
+    const int tid = threadIdx.x;
+    int len = 0, np = 0, ns = 0;
+    if (tid < B) {
+        len = A.seq_lens[tid];
+        np = (max(0, min(len, A.max_pages * kPage)) + kPage - 1) / kPage;
+        ns = max(1, splits_of(A, np));   // a sequence without pages still has one unit
+        lens[tid] = len;
+    }
+    // exclusive prefix of the unit counts (Hillis-Steele in LDS)
+    scan[tid] = ns;
+    __syncthreads();
+    for (int o = 1; o < kUnitSortThreads; o <<= 1) {
+        const int v = tid >= o ? scan[tid - o] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const int total = scan[kUnitSortThreads - 1];
+    const int first = scan[tid] - ns;
+    int P = 1;
+    while (P < total) P <<= 1;
+    for (int j = 0; j < ns; ++j) {
+        const int size = min(np, split_start(A, j + 1)) - split_start(A, j);
+        key[first + j] = ((uint64_t)(0xFFFFF - size) << 36) | ((uint64_t)(0xFFFF - j) << 16) | (uint64_t)tid;
+    }
+    for (int i = total + tid; i < P; i += kUnitSortThreads) key[i] = ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < P; i += kUnitSortThreads) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint64_t a = key[i], b = key[l];
+                    const bool up = (i & k) == 0;
+                    if ((a > b) == up) {
+                        key[i] = b;
+                        key[l] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = tid; i < nslots; i += kUnitSortThreads) {
+        int2 e = make_int2(-1, 0);
+        if (i < total) {
+            const uint64_t kk = key[i];
+            const int sq = (int)(kk & 0xFFFF), sp = 0xFFFF - (int)((kk >> 16) & 0xFFFF);
+            e = make_int2((sq << 16) | sp, lens[sq]);
+        }
+        A.unit_table[i] = e;
+    }
+}
+
 hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s) {
     if (B == 0) return hipSuccess;
+    if (a.compact) {
+        hipLaunchKernelGGL(k_unit_order, dim3(1), dim3(kUnitSortThreads), 0, s, a, B, B * a.nsplit);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const dim3 grid((unsigned)a.hkv, (unsigned)B, (unsigned)a.nsplit);
     int tb = 0;
     // single-tier pools at a fixed page stride take the tier-specialised kernel

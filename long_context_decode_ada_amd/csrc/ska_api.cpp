@@ -47,6 +47,8 @@ struct ska_cache {
     size_t ws_rows = 0;
     uint32_t *d_cnt = nullptr;
     size_t cnt_n = 0;
+    // the unit order of a batch that runs in several rounds (k_unit_order)
+    int2 *d_units = nullptr;
     // stream of the last decode call (calls share the workspace) and the
     // event that orders a call on another stream after it
     mutable hipStream_t last_stream = nullptr;
@@ -101,11 +103,12 @@ bool same_shape(const ska_pool_desc &a, const ska_pool_desc &b) {
 // the big ones go first and the small ones fill the last round: splits of
 // kTailBase, kTailBase, 2 kTailBase, ... pages, doubling up to at most
 // kTailBase << kTailMaxDoublings pages (and max_pages), handed out largest
-// first; with a batch of at most kCompactMaxBatch the grid is also compacted
-// (each workgroup finds its unit from the lengths, so no slot is spent on a
-// split past the end of a short sequence).  Measured on a ragged batch of 64
-// (70..3546 pages) against four equal splits: 442 -> 387 us; a uniform batch
-// of 64 x 2048 pages within 1 %.
+// first; with a batch of at most kCompactMaxBatch (and at most kUnitSortMax
+// grid slots) the grid is also compacted: k_unit_order lists the units that
+// hold pages in decreasing size and each workgroup takes its slot's entry, so
+// no slot is spent on a split past the end of a short sequence.  Measured on
+// a ragged batch of 64 (70..3546 pages) against four equal splits: 442 -> 387
+// us with the units in split order, a uniform batch of 64 x 2048 pages within 1 %.
 constexpr int kTailBase = 256, kTailMaxDoublings = 3;
 struct SplitLayout {
     int pps = 0, split_m = 0, nsplit = 0;
@@ -251,6 +254,7 @@ void release(ska_cache *c) {
     (void)hipFree(c->d_err);
     (void)hipFree(c->d_ws);
     (void)hipFree(c->d_cnt);
+    (void)hipFree(c->d_units);
     if (c->order_ev) (void)hipEventDestroy(c->order_ev);
     delete c;
 }
@@ -286,6 +290,7 @@ ska_status create(ska_cache **out, const ska_pool_desc *pool) {
     c->cnt_n = (size_t)pool->max_batch * pool->num_kv_heads;
     if (e == hipSuccess) e = hipMalloc((void **)&c->d_cnt, c->cnt_n * sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(c->d_cnt, 0, c->cnt_n * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMalloc((void **)&c->d_units, kUnitSortMax * sizeof(int2));
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->order_ev, hipEventDisableTiming);
     if (e != hipSuccess) {
         release(c);
@@ -480,7 +485,7 @@ ska_status prepare_decode(const ska_cache *c, const uint16_t *k_dense, const flo
     da.max_pages = max_pages;
     da.pps = L.pps;
     da.split_m = L.split_m;
-    da.compact = (L.rounds && batch <= kCompactMaxBatch) ? 1 : 0;
+    da.compact = (L.rounds && batch <= kCompactMaxBatch && (int64_t)batch * L.nsplit <= kUnitSortMax) ? 1 : 0;
     da.nsplit = L.nsplit;
     da.tier_mask = c->pool.tier_mask;
     da.nt = c->nt;
@@ -509,6 +514,7 @@ ska_status decode_impl(const ska_cache *c, const uint16_t *k_dense, const float 
     da.part_o = (float *)ws;
     da.part_ml = (float *)(ws + ws_off_ml(c->ws_rows, d));
     da.counters = c->d_cnt;
+    da.unit_table = da.compact ? c->d_units : nullptr;
     hipStream_t s = (hipStream_t)stream;
     // calls share the workspace: one on another stream waits for the last
     if (s != c->last_stream) {
@@ -538,7 +544,8 @@ namespace {
 constexpr size_t kScratchBytes = (size_t)16 << 20;                  // 16 MiB per GPU
 constexpr size_t kScratchCounters = 65536;                          // (sequence, KV head) merge counters
 constexpr size_t kScratchCounterBytes = kScratchCounters * sizeof(uint32_t);
-constexpr size_t kScratchPartialBytes = kScratchBytes - kScratchCounterBytes;
+constexpr size_t kScratchUnitBytes = kUnitSortMax * sizeof(int2);   // the unit order table
+constexpr size_t kScratchPartialBytes = kScratchBytes - kScratchCounterBytes - kScratchUnitBytes;
 constexpr int kScratchMaxDevices = 64;
 }  // namespace
 
@@ -589,8 +596,10 @@ ska_status ska_decode_attention_noalloc(const ska_cache *c, const float *q, int 
     char *base = nullptr;
     if ((st = scratch_base(c->device, s, &base)) != SKA_OK) return st;
     da.counters = reinterpret_cast<uint32_t *>(base);
-    da.part_o = reinterpret_cast<float *>(base + kScratchCounterBytes);
-    da.part_ml = reinterpret_cast<float *>(base + kScratchCounterBytes + ws_off_ml(rows, d));
+    da.unit_table = da.compact ? reinterpret_cast<int2 *>(base + kScratchCounterBytes) : nullptr;
+    char *parts = base + kScratchCounterBytes + kScratchUnitBytes;
+    da.part_o = reinterpret_cast<float *>(parts);
+    da.part_ml = reinterpret_cast<float *>(parts + ws_off_ml(rows, d));
     if (launch_decode(da, d, G, batch, s) != hipSuccess) return SKA_ERR_HIP;
     return SKA_OK;
 }

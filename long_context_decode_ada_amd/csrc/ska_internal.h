@@ -81,6 +81,9 @@ struct EncodeArgs {
 
 // largest batch whose lengths every decode workgroup reads to find its unit
 constexpr int kCompactMaxBatch = 512;
+// grid slots (batch x splits) one k_unit_order workgroup orders: its 8-byte
+// sort keys fill 128 KiB of LDS; a larger batch is not compacted
+constexpr int kUnitSortMax = 16384;
 
 struct DecodeArgs {
     const uint8_t *kcode;
@@ -110,8 +113,11 @@ struct DecodeArgs {
     int split_m;             // split sizes: pps, pps, 2 pps, ..., pps << split_m, then
                              // pps << split_m each (0: every split has pps pages)
     int nsplit;
-    int compact;             // 1: workgroup slots map to the (sequence, split) units
-                             // with pages, largest splits first (batch <= kCompactMaxBatch)
+    int compact;             // 1: workgroup slots map to the (sequence, split) units in
+                             // decreasing size, through unit_table (batch <= kCompactMaxBatch,
+                             // batch x nsplit <= kUnitSortMax)
+    int2 *unit_table;        // compact: slot -> (sequence << 16 | split, the sequence's
+                             // length), written by k_unit_order; -1 past the last unit
     uint32_t tier_mask;
     int nt;
     int8_t tslot[9];         // tier b -> index among the tiers present

@@ -49,6 +49,34 @@ def test_noalloc_decode_matches_the_decode_and_the_oracle():
     cache.free()
 
 
+def test_noalloc_multi_round_batch_matches_the_decode():
+    """A ragged batch that runs in several rounds (compacted grid, units in
+    decreasing size through the unit table, which the no-alloc call keeps in
+    its static array): equal to ska_decode_attention, two calls in a row."""
+    import torch
+    from long_context_decode_ada_amd import ska
+    dev = "cuda"
+    w = W.make("ragged_b64", 1 / 16)
+    pools = ska.DevicePools.for_workload(w, device=dev)
+    cache = ska.Cache(pools)
+    ska.encode_keys(cache, torch.from_numpy(w.keys).to(dev), torch.from_numpy(w.values.view(np.int16)).to(dev),
+                    torch.from_numpy(w.slot).to(dev))
+    q = torch.from_numpy(w.q).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    for B in (w.B, w.B // 2):
+        say("[noalloc] ragged_b64 1/16, B=%d" % B)
+        sl = torch.from_numpy(np.ascontiguousarray(w.seq_lens[:B])).to(dev)
+        out_na = torch.full((B, w.hq, w.d), float("nan"), device=dev)
+        ska.decode_attention_noalloc(cache, q[:B].contiguous(), bt[:B].contiguous(), sl, out=out_na)
+        out_ref = ska.decode_attention(cache, q[:B].contiguous(), bt[:B].contiguous(), sl)
+        torch.cuda.synchronize()
+        a, b = out_na.cpu().numpy(), out_ref.cpu().numpy()
+        assert np.isfinite(a).all()
+        assert np.array_equal(a, b)
+    assert ska.device_errors(cache) == 0
+    cache.free()
+
+
 def test_noalloc_rejects_a_workspace_beyond_its_array():
     import torch
     from long_context_decode_ada_amd import ska
