@@ -107,9 +107,17 @@ bool same_shape(const ska_pool_desc &a, const ska_pool_desc &b) {
 // grid slots) the grid is also compacted: k_unit_order lists the units that
 // hold pages in decreasing size and each workgroup takes its slot's entry, so
 // no slot is spent on a split past the end of a short sequence.  Measured on
-// a ragged batch of 64 (70..3546 pages) against four equal splits: 442 -> 387
-// us with the units in split order, a uniform batch of 64 x 2048 pages within 1 %.
-constexpr int kTailBase = 256, kTailMaxDoublings = 3;
+// a ragged batch of 64 (70..3546 pages): four equal splits 442 us; splits of
+// 256, 256, 512, 1024, then 2048 pages in split order 387 us, in size order
+// 354 us; 384, 384, then 768 each in size order 345 us (a batch of 160 at
+// half the lengths: 490 -> 477 us; 512, 512, 1024: 348 and 474 us).
+#ifndef SKA_TAIL_BASE
+#define SKA_TAIL_BASE 384
+#endif
+#ifndef SKA_TAIL_DOUBLINGS
+#define SKA_TAIL_DOUBLINGS 1
+#endif
+constexpr int kTailBase = SKA_TAIL_BASE, kTailMaxDoublings = SKA_TAIL_DOUBLINGS;
 struct SplitLayout {
     int pps = 0, split_m = 0, nsplit = 0;
     bool rounds = false;

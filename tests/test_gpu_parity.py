@@ -205,20 +205,20 @@ def test_more_splits_than_one_merge_round():
 
 def test_multi_round_batch_split_layout():
     """A batch whose (sequence, KV head) groups alone fill the CUs runs in
-    rounds of workgroups: by default its splits double in size from 256
-    pages and the grid is compacted (each workgroup finds its unit from the
-    lengths).  Ragged lengths up to 1024 pages, with an empty row, a
-    one-token row and rows on and next to the split boundaries (256, 512
-    pages), match the oracle, and equal splits give the same output."""
-    w = W.make("ragged_b64", 1 / 4, batch=40)                 # 40 x 8 groups, up to 16384 tokens
+    rounds of workgroups: by default its splits are 384, 384, then 768 pages
+    each, handed out in decreasing size through the unit table.  Ragged
+    lengths up to 1773 pages, with an empty row, a one-token row and rows on
+    and next to the split boundaries (384, 768 pages; the longest row crosses
+    1536), match the oracle, and equal splits give the same output."""
+    w = W.make("ragged_b64", 1 / 2, batch=40)                 # 40 x 8 groups, up to 28360 tokens
     lens = w.seq_lens.copy()
     order = np.argsort(-lens, kind="stable")                   # longest first
-    for i, n in zip(order[1:5], [512 * 16 + 16, 512 * 16 - 1, 256 * 16 + 1, 256 * 16]):
+    for i, n in zip(order[1:5], [768 * 16 + 16, 768 * 16 - 1, 384 * 16 + 1, 384 * 16]):
         assert lens[i] >= n
         lens[i] = n
     lens[order[-1]], lens[order[-2]] = 0, 1
     say("[rounds] B=%d max_pages=%d lengths %s" % (w.B, w.max_pages, lens.tolist()))
-    assert lens.max() > 512 * 16
+    assert lens.max() > 1536 * 16
     rng = O.calibrate(w.keys)
     g = gpu_run(w, seq_lens=lens)
     o = oracle_run(w, rng, seq_lens=lens)
