@@ -229,12 +229,12 @@ def test_multi_round_batch_split_layout():
     assert np.abs(g4["out"] - g["out"]).max() < 1e-4
 
 
-@pytest.mark.parametrize("scale,batch", [(1 / 8, 130), (1 / 512, 600)])
+@pytest.mark.parametrize("scale,batch", [(1 / 8, 130), (1 / 32, 512), (1 / 512, 600)])
 def test_multi_round_batches_past_one_wave_of_lengths(scale, batch):
-    """Multi-round batches of 130 sequences (compacted grid, units in size
-    order through the unit table) and of 600 short sequences, past the
-    compaction limit of 512 (the multi-round layout without compaction).
-    Both match the oracle."""
+    """Multi-round batches of 130 sequences and of 512, the compaction limit
+    (compacted grid, units in size order through the unit table), and of 600
+    short sequences, past it (the multi-round layout without compaction).
+    All match the oracle."""
     w = W.make("ragged_b64", scale, batch=batch)
     say("[rounds] B=%d max_pages=%d tokens=%d" % (w.B, w.max_pages, w.n_tokens))
     rng = O.calibrate(w.keys)
