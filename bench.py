@@ -39,7 +39,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["long_context_decode_ada_amd/csrc/k_decode.h", "long_context_decode_ada_amd/csrc/ska_codes.h",
+KERNEL_SOURCES = ["long_context_decode_ada_amd/csrc/k_decode.h", "long_context_decode_ada_amd/csrc/k_decode.hip",
+                  "long_context_decode_ada_amd/csrc/ska_codes.h",
                   "long_context_decode_ada_amd/csrc/ska_internal.h"]
 
 
@@ -197,8 +198,11 @@ def main():
     # about 2 ms, then lowers the clock for about 15 ms before it settles; the
     # untimed settling steps before the W warm-up steps bring each measured
     # path to that steady state (about 45 ms of decode steps).
-    ap.add_argument("--settle", type=int, default=400,
-                    help="untimed steps run back to back before the warm-up of each measured path")
+    ap.add_argument("--settle", type=int, default=0,
+                    help="untimed steps run back to back before the warm-up of each measured path "
+                         "(0: as many as take --settle-ms)")
+    ap.add_argument("--settle-ms", type=float, default=45.0,
+                    help="settling time of each measured path when --settle is 0")
     ap.add_argument("--workload", default="gqa_t32k")
     ap.add_argument("--copies", type=int, default=2, help="pool copies alternated across steps")
     ap.add_argument("--splits", type=int, default=0)
@@ -272,6 +276,21 @@ def main():
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
 
+    def settle_for(fn):
+        """The settling steps of a path: --settle, or as many as take
+        --settle-ms at the path's own step time (timed on a few steps)."""
+        if args.settle > 0:
+            return args.settle
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(5):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return int(math.ceil(args.settle_ms / max(1e-3, ev0.elapsed_time(ev1) / 5)))
+
     def measure(fn, steps, settle):
         """`settle` untimed steps back to back, then the W warm-up steps,
         then EXACTLY `steps` timed steps between two HIP events, bracketed by
@@ -301,16 +320,17 @@ def main():
     # the clock for ~15 ms and settles (per-launch kernel trace; a plain copy
     # kernel shows no such transient, see the design notes).
     ms_cold = measure(run_ada, args.steps, 0)
-    # The metric: `settle` untimed steps bring the GPU to its steady state
-    # under this load, then the W warm-up and the K timed steps.
-    ms_per_step = measure(run_ada, args.steps, args.settle)
+    # The metric: `settle` untimed steps (about 45 ms of this load) bring the
+    # GPU to its steady state, then the W warm-up and the K timed steps.
+    settle = settle_for(run_ada)
+    ms_per_step = measure(run_ada, args.steps, settle)
     # K steps with HIP events around every decode kernel (on the launch
     # stream) for the kernel's own duration, after the same settling: the
     # events of the settling calls are recorded too and dropped.
-    nrec = (args.settle + args.warmup + args.steps + nc - 1) // nc + 1
+    nrec = (settle + args.warmup + args.steps + nc - 1) // nc + 1
     for c in caches:
         ska.profile_begin(c, nrec)
-    for i in range(args.settle):
+    for i in range(settle):
         run_ada(i)
     ms_instrumented = measure(run_ada, args.steps, 0)
     prof = np.concatenate([ska.profile_read(c, nrec)[-((args.steps + nc - 1) // nc):] for c in caches])
@@ -367,8 +387,8 @@ def main():
         # headers (the coded step's bytes without values, query and output)
         code_bytes = step_bytes - qo - res_t * 2 * w.d
         dtd_bytes = code_bytes + res_t * 2 * w.d + dense_bytes
-        ms_dense = float(measure(run_dense, args.steps, args.settle))
-        ms_dtd = float(measure(run_dtd, args.steps, args.settle))
+        ms_dense = float(measure(run_dense, args.steps, settle_for(run_dense)))
+        ms_dtd = float(measure(run_dtd, args.steps, settle_for(run_dtd)))
         log("baselines: dense bf16 %.2f us/step, decompress-then-dot %.2f us/step" % (ms_dense * 1e3, ms_dtd * 1e3))
         baselines = {
             "dense_bf16": {"us_per_step": round(ms_dense * 1e3, 2), "bytes_per_step": int(dense_bytes),
@@ -392,7 +412,7 @@ def main():
         def run_append(i):
             ska.append_decode_attention(caches[i % nc], nk, nv, q, bt, sl, num_splits=args.splits, out=out)
 
-        ms_app = measure(run_append, args.steps, args.settle)
+        ms_app = measure(run_append, args.steps, settle_for(run_append))
         log("decode step with append: %.2f us/step" % (ms_app * 1e3))
         append = {"us_per_step": round(ms_app * 1e3, 2), "extra_us_vs_decode": round((ms_app - ms_per_step) * 1e3, 2)}
 
@@ -426,7 +446,7 @@ def main():
         "kv_tokens_per_s": round(w.n_tokens / (ms_per_step * 1e-3), 1),
         "token_kvhead_per_s": round(w.n_tokens * w.hkv / (ms_per_step * 1e-3), 1),
         "alg_bytes_per_step": int(step_bytes),
-        "settle_steps": args.settle,
+        "settle_steps": settle,
         "cold_start_us_per_step": round(ms_cold * 1e3, 2),
         "config": {"workload": w.name + (" (tier per page and KV head)" if w.head_tiers else ""),
                    "B": w.B, "hq": w.hq, "hkv": w.hkv, "d": w.d,
