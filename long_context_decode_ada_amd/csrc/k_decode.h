@@ -1061,20 +1061,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 
-    if constexpr (APP) {
-        // the wave whose run holds the new token's page stores the token
-        // before it requests any page
-        const int pnew = (len - 1) / kPage;
-        if (pnew >= wp0 && pnew < wp1) {
-            // the page's id: among this wave's staged block-table entries
-            // (one per lane from p0 + wofs) when it is within the first 64
-            const int rel = pnew - (p0 + wofs);
-            const int ph_new = rel < 64 ? __builtin_amdgcn_readlane(ph_raw, rel) : A.block_table[bt_row + pnew];
-            append_token<D, TB>(A, seq, kvh, len_in, ph_new, akey, atau2, c2s, s2s, qT[wave],
-                                reinterpret_cast<uint8_t *>(mo[wave][0]));
-        }
-    }
-
     // The loads of the wave's first pages.  At the start of the kernel every
     // wave of the chip requests its first pages at once, and a wave's requests
     // wait for room in the memory queue (about 2 us here).  The waves that
@@ -1094,6 +1080,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             for (int i = 0; i < kBufs; ++i) load_page<D, TB>(A, dd[i], kvh, R[i]);
         }
     };
+
+    bool loaded = false;
+    if constexpr (APP) {
+        // the wave whose run holds the new token's page stores the token; a
+        // wave that prepares no query requests its first pages first, so
+        // that they are in flight during the store, and requests them again
+        // after it if the new page is among them
+        const int pnew = (len - 1) / kPage;
+        if (pnew >= wp0 && pnew < wp1) {
+            if (!prep_wave) {
+                first_loads();
+                loaded = true;
+            }
+            // the page's id: among this wave's staged block-table entries
+            // (one per lane from p0 + wofs) when it is within the first 64
+            const int rel = pnew - (p0 + wofs);
+            const int ph_new = rel < 64 ? __builtin_amdgcn_readlane(ph_raw, rel) : A.block_table[bt_row + pnew];
+            append_token<D, TB>(A, seq, kvh, len_in, ph_new, akey, atau2, c2s, s2s, qT[wave],
+                                reinterpret_cast<uint8_t *>(mo[wave][0]));
+            if (loaded && pnew - wp0 < kBufs) first_loads();
+        }
+    }
 
     // Query prep, section 2.1's c_q: per tier, the angle codes of each query
     // row and the decoded direction u_a = (prod_{k<a} sin c_k) * cos c_a
@@ -1239,7 +1247,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             ++ti;
         }
         first_loads();
-    } else {
+    } else if (!loaded) {
         first_loads();
     }
     __syncthreads();
