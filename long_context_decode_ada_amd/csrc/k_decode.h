@@ -497,30 +497,22 @@ __device__ __forceinline__ void softmax_pv(const DecodeArgs &A, float lg, int nt
 }
 
 
-// f_b, logits, online softmax and the MFMA P.V update of one page.  DBG also
-// stores the logits (a separate kernel variant, so that the store does not
-// enter the memory-wait accounting of the production loop).
-template <int D, int G, int B, bool DBG, bool QF>
-__device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &r, int ntok, int64_t logit_base,
-                                               const uint32_t (&u)[query_words<D, G, QF>()], float sq, const float2 *__restrict__ lut,
-                                               const float *__restrict__ rlev, float *__restrict__ pb,
-                                               WaveState &st, v4f (&acc)[D / 16]) {
+// The lane's share of f_b on its slice of a page of tier B: the running
+// sine product P over the slice's angles and, per head h, the sum F[h] of
+// u_q,h[a] * (product of the slice's sines before a) * cos of angle a.
+template <int D, int G, int B, bool QF>
+__device__ __forceinline__ void slice_fb(const PageBuf<D> &r, const uint32_t (&u)[query_words<D, G, QF>()],
+                                         const float2 *__restrict__ lut, float (&F)[G], float &P) {
     constexpr int NA = D / 4;
-    constexpr int NT = D / 16;
-    const int lane = threadIdx.x & 63;
-    const int t = lane >> 2, j = lane & 3;
-    const int q4 = lane >> 4, n16 = lane & 15;
-
-    // ---- f_b on the lane's slice ----
+    const int j = threadIdx.x & 3;
     const uint32_t az_base = 8u * ((j == 3) ? lut_azimuth(B) : lut_polar(B));
     const uint32_t pad_base = 8u * ((j == 3) ? kLutOnes : lut_polar(B));
     const char *lutb = reinterpret_cast<const char *>(lut);
     CodeAddr<B> ca;
     ca.init(r.cw);
-    float F[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) F[h] = 0.f;
-    float P = 1.f;
+    P = 1.f;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const uint32_t c8 = ca.at(r.cw, i);
@@ -537,6 +529,18 @@ __device__ __forceinline__ void compute_page_b(const DecodeArgs &A, PageBuf<D> &
             F[h] = query_fma<D, G, QF>(u, e2, w, F[h]);
         }
     }
+}
+
+// The rest of a coded page, the same for every tier: the four slices joined
+// into f_b, the logits, online softmax and the MFMA P.V update.  DBG also
+// stores the logits (a separate kernel variant, so that the store does not
+// enter the memory-wait accounting of the production loop).
+template <int D, int G, bool DBG>
+__device__ __forceinline__ void finish_page(const DecodeArgs &A, PageBuf<D> &r, int ntok, int64_t logit_base,
+                                            const float (&F)[G], float P, float sq, const float *__restrict__ rlev,
+                                            float *__restrict__ pb, WaveState &st, v4f (&acc)[D / 16]) {
+    const int lane = threadIdx.x & 63;
+    const int t = lane >> 2, j = lane & 3;
 
     // ---- join the four slices: C_j = prod_{i<j} S_i ----
     const float C = slice_prefix(P, j);
@@ -622,16 +626,22 @@ __device__ __forceinline__ void compute_page(const DecodeArgs &A, const PageDesc
             return;
         }
         ntok = min(ntok, kPage - (int)(hb >> 4));
-        compute_page_b<D, G, TB, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc);
+        float F[G], P;
+        slice_fb<D, G, TB, QF>(r, u, lut, F, P);
+        finish_page<D, G, DBG>(A, r, ntok, lbase, F, P, sq, rlev, pb, st, acc);
     } else {
+        // only the slice part depends on the tier: the join, the softmax and
+        // the P.V product exist once, after the dispatch
         ntok = min(ntok, pd.cnt);
+        float F[G], P;
         switch (pd.b) {
-            case 2: compute_page_b<D, G, 2, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
-            case 3: compute_page_b<D, G, 3, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
-            case 4: compute_page_b<D, G, 4, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
-            case 6: compute_page_b<D, G, 6, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
-            default: compute_page_b<D, G, 8, DBG, QF>(A, r, ntok, lbase, u, sq, lut, rlev, pb, st, acc); break;
+            case 2: slice_fb<D, G, 2, QF>(r, u, lut, F, P); break;
+            case 3: slice_fb<D, G, 3, QF>(r, u, lut, F, P); break;
+            case 4: slice_fb<D, G, 4, QF>(r, u, lut, F, P); break;
+            case 6: slice_fb<D, G, 6, QF>(r, u, lut, F, P); break;
+            default: slice_fb<D, G, 8, QF>(r, u, lut, F, P); break;
         }
+        finish_page<D, G, DBG>(A, r, ntok, lbase, F, P, sq, rlev, pb, st, acc);
     }
 }
 
