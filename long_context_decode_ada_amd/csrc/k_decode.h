@@ -949,7 +949,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // read with the page's data and checked before the page is used.
     int e_pg = 0, e_phys = -1, e_bits = 0, nvalid = 0;
     uint32_t e_lo = 0, e_hi = 0;
-    auto page_list = [&](int c0, int ph) {
+    // (mixed tiers) the header and the record offset of the lane's page (of
+    // this KV head's records with per-head tiers), read at a clamped (valid)
+    // id; the page list checks them
+    auto page_meta = [&](int c0, int ph, int &hdr, uint64_t &off) {
+        const bool ok = lane < min(64, wp1 - c0) && ph >= 0 && (int64_t)ph < A.num_pages;
+        const int phc = ok ? ph : 0;
+        const int64_t hix = A.head_tiers ? (int64_t)phc * A.hkv + kvh : (int64_t)phc;
+        hdr = (int)A.page_bits[hix];
+        off = A.page_off ? A.page_off[hix] : (uint64_t)phc * (uint64_t)A.page_stride;
+    };
+    auto page_list = [&](int c0, int ph, int hdr, uint64_t off) {
         const int cn = min(64, wp1 - c0);
         e_pg = c0 + lane;
         e_phys = -1;
@@ -963,13 +973,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             e_phys = ok ? ph : -1;
             key = ok ? TB : 15;
         } else {
-            // header and offset of the page (of this KV head's records with
-            // per-head tiers), read at a clamped (valid) id
-            const int phc = ok ? ph : 0;
-            const int64_t hix = A.head_tiers ? (int64_t)phc * A.hkv + kvh : (int64_t)phc;
-            const int hdr = (int)A.page_bits[hix];
             const int bb = hdr & 15;   // tier bits; the high four count empty slots
-            const uint64_t off = A.page_off ? A.page_off[hix] : (uint64_t)phc * (uint64_t)A.page_stride;
             const bool okb = ok && bb >= 2 && bb <= 8 && ((A.tier_mask >> bb) & 1u);
             if (ok && !okb) atomicOr(A.err, 4u);
             e_phys = okb ? ph : -1;
@@ -1031,13 +1035,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
             load_page<D, TB>(A, dd[i], kvh, R[i]);
         }
     };
-    auto start_chunk = [&](int c0, int ph) {
-        page_list(c0, ph);
-        issue_chunk();
-    };
-    // (pools of mixed tiers build the first chunk's page list before the
-    // query preparation and issue its page loads after it: two page buffers
-    // held across the preparation would spill)
+    // (pools of mixed tiers request the first chunk's headers and offsets
+    // before the query preparation, and list and request its pages after
+    // it: two page buffers held across the preparation would spill)
+    int m_hdr = 0;
+    uint64_t m_off = 0;
     // Single tier: the wave walks its pages in order, reading the block
     // table 64 entries (one per lane) at a time into two rotating register
     // slots, the next slot always requested a chunk ahead; the page loads
@@ -1070,6 +1072,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    if constexpr (TB == 0) page_meta(wp0, ph_first, m_hdr, m_off);
 
     // The loads of the wave's first pages.  At the start of the kernel every
     // wave of the chip requests its first pages at once, and a wave's requests
@@ -1358,7 +1361,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     }
     int ph_next = -1;   // the next chunk's block-table entries, requested a chunk ahead
     for (int c0 = wp0; TB == 0 && c0 < wp1; c0 += 64) {
-        start_chunk(c0, c0 == wp0 ? ph_first : ph_next);
+        if (c0 != wp0) page_meta(c0, ph_next, m_hdr, m_off);   // (the first chunk's: before the preparation)
+        page_list(c0, c0 == wp0 ? ph_first : ph_next, m_hdr, m_off);
+        issue_chunk();
         ph_next = bt_raw(c0 + 64);
         ph_next = (c0 + 64 + lane < wp1) ? ph_next : -1;   // (all -1 past the wave's run)
         if (nvalid == 0) continue;
