@@ -1458,7 +1458,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     // count rounded up to a power of two (at least 4), are issued, with
     // indices past the last split clamped to it.  (Fewer in the mixed-tier
     // kernel, whose register file is full.)
-    constexpr int kMergeFast = TB == 0 ? 8 : 32;
+    constexpr int kMergeFast = (TB == 0 && QF) ? 8 : 32;   // (the binary32-direction mixed-tier kernel: fewer registers)
     static_assert(D % 64 == 0, "a wave's merge elements share one head");
     auto merge_fast = [&](auto n_c) {
         constexpr int N = decltype(n_c)::value;

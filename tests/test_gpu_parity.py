@@ -78,21 +78,23 @@ def test_split_count_and_determinism():
             assert np.abs(g["out"] - base["out"]).max() < 1e-4
 
 
-@pytest.mark.parametrize("name,scale,counts", [
+@pytest.mark.parametrize("name,scale,counts,qprec", [
     # 128 pages per row: explicit counts giving 4, 5, 8, 9, 16, 19, 32 and 43
     # non-empty splits, on both sides of each size of the one-round merge
     # (4, 8, 16, 32 loads per thread) and past it (the LDS weight pass)
-    ("gqa_t32k", 1 / 16, (4, 5, 8, 9, 16, 19, 32, 43)),
-    # the mixed-tier kernel merges up to 8 splits in one round
-    ("mixed_tiers", 1 / 8, (5, 8, 9, 12)),
+    ("gqa_t32k", 1 / 16, (4, 5, 8, 9, 16, 19, 32, 43), 0),
+    ("mixed_tiers", 1 / 8, (4, 5, 8, 9, 16, 19, 32, 43), 0),
+    # the mixed-tier kernel with binary32 directions (query_precision 1) merges
+    # up to 8 splits in one round
+    ("mixed_tiers", 1 / 8, (5, 8, 9, 12), 1),
 ])
-def test_merge_paths_at_their_split_count_boundaries(name, scale, counts):
+def test_merge_paths_at_their_split_count_boundaries(name, scale, counts, qprec):
     w = W.make(name, scale, batch=2)
     rng = O.calibrate(w.keys)
     o = oracle_run(w, rng)
     base = None
     for ns in counts:
-        g = gpu_run(w, num_splits=ns, repeat=2)
+        g = gpu_run(w, num_splits=ns, repeat=2, query_precision=qprec)
         assert np.array_equal(g["outs"][0], g["outs"][1]), "run-to-run difference at %d splits" % ns
         compare(w, g, o, rng, label="%s splits=%d" % (name, ns))
         if base is None:
