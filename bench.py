@@ -11,9 +11,11 @@ alternated so that the 256 MB Infinity Cache cannot serve one step's pages to
 the next.  Each measured path first runs --settle untimed steps back to back
 (the GPU's clock controller needs about 20 ms of this load to settle after an
 idle period), then the W warm-up steps, then the K timed steps,
-uninstrumented; a further pass records HIP events around every decode kernel
-for its own duration.  The line also reports the K steps timed right after
-the encode, before any settling (cold_start_us_per_step).
+uninstrumented; a further pass, settled the same way, times the decode
+kernel itself: one more HIP event after its first step, and the span of the
+K-1 calls after it, which run back to back.  The line also reports the K
+steps timed right after the encode, before any settling
+(cold_start_us_per_step).
 
 dtype: the step computes in binary32 (logits, softmax, accumulation) with the
 query direction entering f_b as binary16 and the values and probabilities
@@ -307,6 +309,27 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / steps
 
+    evm = torch.cuda.Event(enable_timing=True)
+
+    def kernel_span(fn, steps, settle):
+        """As measure(), with one more event after the first timed step:
+        ms per step over the steps after it."""
+        for i in range(settle):
+            fn(i)
+        for i in range(args.warmup):
+            fn(settle + i)
+        torch.cuda.synchronize()
+        ev0.record()
+        fn(0)
+        evm.record()
+        for i in range(1, steps):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        if steps < 2:
+            return ev0.elapsed_time(ev1)
+        return evm.elapsed_time(ev1) / (steps - 1)
+
     # one decode step per call; its arguments are checked and marshalled once,
     # here, so that a timed step enqueues only the library call
     ada_calls = [ska.prepared_decode(c, q, bt, sl, out, num_splits=args.splits) for c in caches]
@@ -324,21 +347,18 @@ def main():
     # GPU to its steady state, then the W warm-up and the K timed steps.
     settle = settle_for(run_ada)
     ms_per_step = measure(run_ada, args.steps, settle)
-    # K steps with HIP events around every decode kernel (on the launch
-    # stream) for the kernel's own duration, after the same settling: the
-    # events of the settling calls are recorded too and dropped.
-    nrec = (settle + args.warmup + args.steps + nc - 1) // nc + 1
-    for c in caches:
-        ska.profile_begin(c, nrec)
-    for i in range(settle):
-        run_ada(i)
-    ms_instrumented = measure(run_ada, args.steps, 0)
-    prof = np.concatenate([ska.profile_read(c, nrec)[-((args.steps + nc - 1) // nc):] for c in caches])
-    for c in caches:
-        ska.profile_begin(c, 0)
-    k_ms = float(prof.mean())
-    log("timed %d steps: %.2f us/step (cold start: %.2f); with per-kernel events %.2f us/step, decode kernel "
-        "%.2f us" % (args.steps, ms_per_step * 1e3, ms_cold * 1e3, ms_instrumented * 1e3, k_ms * 1e3))
+    # The decode kernel's own average duration, after the same settling and
+    # warm-up: K steps between HIP events on the launch stream, with one
+    # more event after the first step.  The K-1 calls after that event run
+    # back to back (in the kernel trace one kernel starts as the previous
+    # ends), so their span divided by K-1 is the kernel's average launch
+    # duration without the latency of the first launch after the start
+    # event.  (An event pair around every kernel would add each marker's
+    # dispatch latency, about 5 us, to every launch.)  With a unit-order
+    # kernel in the step (batches of several rounds) the span covers it too.
+    k_ms = kernel_span(run_ada, args.steps, settle)
+    log("timed %d steps: %.2f us/step (cold start: %.2f); decode kernel %.2f us (back to back, HIP events)"
+        % (args.steps, ms_per_step * 1e3, ms_cold * 1e3, k_ms * 1e3))
     if not np.isfinite(out.cpu().numpy()).all():
         log("non-finite output")
         sys.exit(1)
@@ -361,7 +381,7 @@ def main():
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": "k_decode<d=%d,G=%d>" % (w.d, w.hq // w.hkv), "kernel_us": round(k_ms * 1e3, 2),
-            "kernel_us_p10_p50_p90": [round(float(np.percentile(prof, p)) * 1e3, 2) for p in (10, 50, 90)],
+            "kernel_us_method": "HIP events: span of K-1 back-to-back calls after the first timed one",
             "alg_bytes_per_launch": int(kb)}
 
     baselines = None

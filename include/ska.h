@@ -323,8 +323,11 @@ ska_status ska_device_errors(ska_cache *cache, void *stream, uint32_t *flags_out
  * traffic per generated token): ska_profile_begin makes the next `max_calls`
  * ska_decode_attention calls on this cache record two HIP events on their
  * stream, around the decode kernel (query preparation, paged decode and split
- * merge); 0 stops recording.  The events skip the system-scope fence, so they
- * barely perturb back-to-back calls.  ska_profile_read waits for the recorded
+ * merge); 0 stops recording.  The events skip the system-scope fence, but
+ * each pair still adds its markers' dispatch latency to the gap between calls
+ * and to the recorded figure (a few microseconds per call on MI355X); for the
+ * average of back-to-back calls, time a run of calls between two events
+ * instead.  ska_profile_read waits for the recorded
  * events and writes ms_out[i] for call i, *n_out = calls recorded (at most
  * max_calls). */
 ska_status ska_profile_begin(ska_cache *cache, int max_calls);

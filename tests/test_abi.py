@@ -225,3 +225,32 @@ def test_prepared_decode_call_matches_the_plain_call():
         ska.prepared_decode(cache, q, bt, sl, out[:1])
     assert ska.device_errors(cache) == 0
     cache.free()
+
+
+@pytest.mark.gpu
+def test_profile_records_one_duration_per_decode_call():
+    """ska_profile_begin/ska_profile_read: one finite positive duration per
+    decode call while recording is on, none after it is turned off, and the
+    outputs unchanged by the events."""
+    import numpy as np
+    import torch
+    from long_context_decode_ada_amd import workloads as W
+    w = W.make("gqa_t32k", 1 / 64, batch=2)
+    dev = "cuda"
+    cache = ska.Cache(ska.DevicePools.for_workload(w, device=dev))
+    ska.encode_keys(cache, torch.from_numpy(w.keys).to(dev), torch.from_numpy(w.values.view(np.int16)).to(dev),
+                    torch.from_numpy(w.slot).to(dev))
+    q = torch.from_numpy(w.q).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    ref = ska.decode_attention(cache, q, bt, sl)
+    ska.profile_begin(cache, 8)
+    outs = [ska.decode_attention(cache, q, bt, sl) for _ in range(3)]
+    ms = ska.profile_read(cache, 8)
+    assert ms.shape == (3,) and np.all(np.isfinite(ms)) and np.all(ms > 0), ms
+    assert all(torch.equal(o, ref) for o in outs)
+    ska.profile_begin(cache, 0)
+    ska.decode_attention(cache, q, bt, sl)
+    assert ska.profile_read(cache, 8).shape == (0,)
+    assert ska.device_errors(cache) == 0
+    cache.free()
