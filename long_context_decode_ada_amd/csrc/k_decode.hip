@@ -279,18 +279,22 @@ hipError_t launch_decompress(const DecodeArgs &a, int d, int B, hipStream_t s) {
 // Handed out in decreasing size, neighbouring slots hold units of similar
 // size and the engines fill and drain together.  One workgroup: the units of
 // each sequence (as the decode splits it) get the key (size descending, split
-// descending, sequence), unique, so the order is the same on every call; a
-// bitonic sort in LDS; then slot i of the table receives the i-th unit and
-// its sequence's length (-1 past the last unit).  Which workgroup computes a
-// unit does not change the unit's result, so the outputs do not depend on
-// the order.
+// descending, sequence), unique, so the order is the same on every call;
+// slot i of the table receives the unit of the i-th smallest key and its
+// sequence's length (-1 past the last unit).  Up to kUnitRankMax units, each
+// unit's slot is the number of keys below its own (one pass over the keys in
+// LDS, read by every lane of a wave at once); more units are sorted with a
+// bitonic network in LDS.  Which workgroup computes a unit does not change
+// the unit's result, so the outputs do not depend on the order.
 constexpr int kUnitSortThreads = 1024;
+constexpr int kUnitRankMax = kUnitSortThreads;
 static_assert(kCompactMaxBatch <= kUnitSortThreads, "one thread per sequence");
+static_assert(kUnitRankMax % 2 == 0 && kUnitRankMax < kUnitSortMax, "pairs of keys, one key per thread");
 __global__ __launch_bounds__(kUnitSortThreads) void k_unit_order(DecodeArgs A, int B, int nslots) {
-    __shared__ uint64_t key[kUnitSortMax];
-    __shared__ int scan[kUnitSortThreads];
+    __shared__ __attribute__((aligned(16))) uint64_t key[kUnitSortMax];
+    __shared__ int wsum[kUnitSortThreads / 64];
     __shared__ int lens[kCompactMaxBatch];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int len = 0, np = 0, ns = 0;
     if (tid < B) {
         len = A.seq_lens[tid];
@@ -298,23 +302,50 @@ __global__ __launch_bounds__(kUnitSortThreads) void k_unit_order(DecodeArgs A, i
         ns = max(1, splits_of(A, np));   // a sequence without pages still has one unit
         lens[tid] = len;
     }
-    // exclusive prefix of the unit counts (Hillis-Steele in LDS)
-    scan[tid] = ns;
-    __syncthreads();
-    for (int o = 1; o < kUnitSortThreads; o <<= 1) {
-        const int v = tid >= o ? scan[tid - o] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+    // exclusive prefix of the unit counts: a scan within each wave, then the
+    // waves' totals
+    int incl = ns;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        incl += lane >= o ? v : 0;
     }
-    const int total = scan[kUnitSortThreads - 1];
-    const int first = scan[tid] - ns;
-    int P = 1;
-    while (P < total) P <<= 1;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int total = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < kUnitSortThreads / 64; ++w) {
+        const int t = wsum[w];
+        total += t;
+        before += w < wave ? t : 0;
+    }
+    const int first = before + incl - ns;
     for (int j = 0; j < ns; ++j) {
         const int size = min(np, split_start(A, j + 1)) - split_start(A, j);
         key[first + j] = ((uint64_t)(0xFFFFF - size) << 36) | ((uint64_t)(0xFFFF - j) << 16) | (uint64_t)tid;
     }
+    auto unit_of = [&](uint64_t kk) {
+        const int sq = (int)(kk & 0xFFFF), sp = 0xFFFF - (int)((kk >> 16) & 0xFFFF);
+        return make_int2((sq << 16) | sp, lens[sq]);
+    };
+    if (total <= kUnitRankMax) {
+        if (tid == 0 && (total & 1)) key[total] = ~0ull;   // (pairs: a key above every unit's)
+        __syncthreads();
+        if (tid < total) {
+            const uint64_t k = key[tid];
+            const ulonglong2 *kp = reinterpret_cast<const ulonglong2 *>(key);
+            int rank = 0;
+            for (int v = 0; v < (total + 1) / 2; ++v) {
+                const ulonglong2 kk = kp[v];
+                rank += (kk.x < k ? 1 : 0) + (kk.y < k ? 1 : 0);
+            }
+            A.unit_table[rank] = unit_of(k);
+        }
+        for (int i = total + tid; i < nslots; i += kUnitSortThreads) A.unit_table[i] = make_int2(-1, 0);
+        return;
+    }
+    int P = 1;
+    while (P < total) P <<= 1;
     for (int i = total + tid; i < P; i += kUnitSortThreads) key[i] = ~0ull;
     __syncthreads();
     for (int k = 2; k <= P; k <<= 1) {
@@ -333,15 +364,7 @@ __global__ __launch_bounds__(kUnitSortThreads) void k_unit_order(DecodeArgs A, i
             __syncthreads();
         }
     }
-    for (int i = tid; i < nslots; i += kUnitSortThreads) {
-        int2 e = make_int2(-1, 0);
-        if (i < total) {
-            const uint64_t kk = key[i];
-            const int sq = (int)(kk & 0xFFFF), sp = 0xFFFF - (int)((kk >> 16) & 0xFFFF);
-            e = make_int2((sq << 16) | sp, lens[sq]);
-        }
-        A.unit_table[i] = e;
-    }
+    for (int i = tid; i < nslots; i += kUnitSortThreads) A.unit_table[i] = i < total ? unit_of(key[i]) : make_int2(-1, 0);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int d, int G, int B, hipStream_t s) {
