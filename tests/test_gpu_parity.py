@@ -246,27 +246,30 @@ def test_multi_round_batches_past_one_wave_of_lengths(scale, batch):
     compare(w, g, o, rng, label="rounds B=%d" % batch)
 
 
-@pytest.mark.parametrize("batch", [256, 257, 512])
-def test_multi_round_batches_of_one_row_repeated(batch):
-    """`batch` rows over the same 2048 pages with the same query rows (one
-    block-table row of long_t128k at 1/4 repeated): a multi-round batch of
-    4 units per row, 1024 units at 256 rows (the most the unit-order kernel
-    ranks by counting), 1028 and 2048 units past that (its bitonic sort, with
-    and without padding keys).  Every row matches the oracle's decode of the
-    row, and all rows are equal bit for bit (the same computation on the same
-    inputs, whichever workgroups ran it)."""
+@pytest.mark.parametrize("batch,pages", [(256, 2048), (257, 2048), (512, 2048), (255, 1024)])
+def test_multi_round_batches_of_one_row_repeated(batch, pages):
+    """`batch` rows over the same pages with the same query rows (one
+    block-table row of long_t128k at 1/4 repeated, read to `pages` pages): a
+    multi-round batch of 4 units per row at 2048 pages (splits of 384, 384,
+    768, 512), 3 at 1024.  1024 units at 256 rows are the most the
+    unit-order kernel ranks by counting, 765 an odd count of them; 1028 and
+    2048 units go through its bitonic sort, with and without padding keys.
+    Every row matches the oracle's decode of the row, and all rows are equal
+    bit for bit (the same computation on the same inputs, whichever
+    workgroups ran it)."""
     import dataclasses
     base = W.make("long_t128k", 1 / 4)
     assert base.B == 1 and int(base.seq_lens[0]) == 2048 * W.PAGE
+    lens1 = np.array([pages * W.PAGE], np.int32)
     w = dataclasses.replace(base, B=batch, block_table=np.repeat(base.block_table, batch, 0),
-                            seq_lens=np.repeat(base.seq_lens, batch), q=np.repeat(base.q, batch, 0))
+                            seq_lens=np.repeat(lens1, batch), q=np.repeat(base.q, batch, 0))
     rng = O.calibrate(base.keys)
-    o1 = oracle_run(base, rng, want_logits=False)
+    o1 = oracle_run(base, rng, want_logits=False, seq_lens=lens1)
     g = gpu_run(w, want_logits=False)
     assert g["errors"] == 0
     assert np.array_equal(g["out"], np.repeat(g["out"][:1], batch, 0)), "rows differ"
     o = {"out": np.repeat(o1["out"], batch, 0), "logits": None, "pools": o1["pools"]}
-    compare(w, g, o, rng, label="%d rows of one row repeated" % batch)
+    compare(w, g, o, rng, label="%d rows of one %d-page row repeated" % (batch, pages))
 
 
 @pytest.mark.parametrize("name,scale,batch", [("gqa_t32k", 1 / 16, None), ("mixed_tiers", 1 / 16, 4)])
