@@ -6,6 +6,8 @@ drawn per case, and so is the precision of the query direction (binary16 or
 binary32).  Every case checks the encode bit for bit and the decode
 (outputs and logits) against the oracle; every other case also runs the
 decode step with append."""
+import os
+
 import numpy as np
 import pytest
 
@@ -77,7 +79,11 @@ def _case(seed):
     return w, splits, qmode, qprec
 
 
-@pytest.mark.parametrize("seed", range(40))
+# 40 seeds by default; SKA_RANDOM_SEEDS=<n> runs seeds 0..n-1 (a longer sweep)
+NSEEDS = int(os.environ.get("SKA_RANDOM_SEEDS", "40"))
+
+
+@pytest.mark.parametrize("seed", range(NSEEDS))
 def test_random_shape_parity(seed):
     w, splits, qmode, qprec = _case(seed)
     say("[random %d] d=%d hkv=%d G=%d B=%d lens=%s tiers=%s head_tiers=%s packed=%s splits=%d query_mode=%d "
