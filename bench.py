@@ -215,6 +215,8 @@ def main():
                     help="skip the dense-bf16 and decompress-then-dot timings on the same pages")
     ap.add_argument("--head-tiers", action="store_true",
                     help="mixed_tiers only: a tier per (page, KV head) instead of per page")
+    ap.add_argument("--query-precision", choices=("f16", "f32"), default="f16",
+                    help="precision of the query direction inside f_b (the pool's query_precision)")
     ap.add_argument("--no-append", action="store_true",
                     help="skip the timing of the decode step with append (ska_append_decode_attention)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-oracle timing")
@@ -252,8 +254,10 @@ def main():
     vals = torch.from_numpy(w.values.view(np.int16)).to(dev)
     slot = torch.from_numpy(w.slot).to(dev)
     caches, rng = [], None
+    qprec = ska.QDIR_F32 if args.query_precision == "f32" else ska.QDIR_F16
     for c in range(args.copies):
-        pools = ska.DevicePools.for_workload(w, device=dev, poison=False, max_splits=args.splits)
+        pools = ska.DevicePools.for_workload(w, device=dev, poison=False, max_splits=args.splits,
+                                             query_precision=qprec)
         cache = ska.Cache(pools)
         ska.encode_keys(cache, keys, vals, slot, radius_range=rng)
         rng = ska.radius_range(cache)
@@ -377,7 +381,8 @@ def main():
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     kb = decode_kernel_bytes(w)
     ach = float(kb / (k_ms * 1e-3) / 1e9)
-    traffic = read_traffic(w.name)
+    # (the counter summaries cover the binary16-direction kernel)
+    traffic = read_traffic(w.name) if args.query_precision == "f16" else None
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": "k_decode<d=%d,G=%d>" % (w.d, w.hq // w.hkv), "kernel_us": round(k_ms * 1e3, 2),
@@ -460,7 +465,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32+fp16+bf16",
+        "dtype": "fp32+fp16+bf16" if args.query_precision == "f16" else "fp32+bf16",
         "data": "synthetic",
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "kv_tokens_per_s": round(w.n_tokens / (ms_per_step * 1e-3), 1),
@@ -472,7 +477,8 @@ def main():
                    "B": w.B, "hq": w.hq, "hkv": w.hkv, "d": w.d,
                    "T": int(w.seq_lens.max()), "angle_bits": tiers, "radius": "8-bit " +
                    ("log" if w.radius_mode == W.LOG else "uniform"), "page": 16,
-                   "values": "bf16", "pool_copies": nc, "splits": args.splits or "auto"},
+                   "values": "bf16", "pool_copies": nc, "splits": args.splits or "auto",
+                   "query_direction": "binary16" if args.query_precision == "f16" else "binary32"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "baselines": baselines,

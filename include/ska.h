@@ -122,7 +122,9 @@ typedef struct {
                                  which moves a logit by at most 2^-11 (typically ~1e-4 at
                                  d = 128) of its bound scale*|q|*r~; SKA_QDIR_F32 keeps binary32
                                  (for keys with outlier channels, whose large radii turn that
-                                 into large output errors; about 20 % slower) */
+                                 into large output errors; on MI355X about 4 % slower on a
+                                 pool of one tier at d = 128 with 4 query heads per KV head,
+                                 about twice as slow on a pool of mixed tiers) */
     /* Maxima of the decode calls on this cache, fixed when it is created:
        they size the decode workspace (split partials and merge counters),
        which is allocated then and never again.  A decode call outside them

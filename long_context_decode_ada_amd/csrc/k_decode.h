@@ -168,10 +168,17 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&cw)[8], int i) {
 // b = 4, 8 and 2 the codes of each word are first spread (two or four masked
 // shifts per word) so that every 8*code sits in its own byte or half-word and
 // takes one extraction; other widths use a field extract and a shift.
-template <int B>
+// SPREAD = false: plain field extracts, no spread words (for kernels at the
+// register limit, where eight or sixteen more live registers cost more than
+// the extracts they save).
+template <int B, bool SPREAD = true>
 struct CodeAddr {
     uint32_t s[16];
     __device__ __forceinline__ void init(const uint32_t (&cw)[8]) {
+        if constexpr (!SPREAD) {
+            (void)cw;
+            return;
+        }
         constexpr int SW = record_bytes(B == 3 ? 128 : 128, B) / 16;
         if constexpr (B == 4) {
 #pragma unroll
@@ -201,7 +208,9 @@ struct CodeAddr {
         (void)SW;
     }
     __device__ __forceinline__ uint32_t at(const uint32_t (&cw)[8], int i) const {
-        if constexpr (B == 4) {
+        if constexpr (!SPREAD) {
+            return code_at<B>(cw, i) << 3;
+        } else if constexpr (B == 4) {
             const uint32_t w = s[2 * (i >> 3) + (i & 1)];
             return __builtin_amdgcn_ubfe(w, 8 * ((i & 7) >> 1), 8);
         } else if constexpr (B == 8) {
@@ -238,9 +247,10 @@ __device__ __forceinline__ float fma_mix_hi(uint32_t u, float w, float acc) {
 // channels (large radii, a sharp softmax) that logit error, scaled by the
 // radius, moves the outputs by more than theirs.  binary32 takes the same
 // instructions but twice the registers ((d/4 angles) x G heads per lane):
-// at G = 4 the kernels then run at the register limit, where the compiler no
-// longer keeps several table reads in flight (about 20 % slower on a
-// single-tier pool), and the header-dispatched kernel spills.  So binary16
+// at G = 4, d = 128 the kernels run at the register limit, so they extract
+// the codes without spread words (CodeAddr); single-tier pools then decode
+// about 4 % slower than with binary16 (b = 4; 1-2 % at b = 3), while the
+// header-dispatched kernel spills and runs at about half speed.  So binary16
 // is the default and binary32 the precise mode.// 32-bit words of the query direction per lane: (D/4 angles) x G heads
 template <int D, int G, bool QF>
 constexpr int query_words() { return QF ? D * G / 4 : D * G / 8; }
@@ -508,7 +518,8 @@ __device__ __forceinline__ void slice_fb(const PageBuf<D> &r, const uint32_t (&u
     const uint32_t az_base = 8u * ((j == 3) ? lut_azimuth(B) : lut_polar(B));
     const uint32_t pad_base = 8u * ((j == 3) ? kLutOnes : lut_polar(B));
     const char *lutb = reinterpret_cast<const char *>(lut);
-    CodeAddr<B> ca;
+    // binary32 words of four heads at d = 128 fill the register file: no spread words there
+    CodeAddr<B, !(QF && G * D >= 512)> ca;
     ca.init(r.cw);
 #pragma unroll
     for (int h = 0; h < G; ++h) F[h] = 0.f;
