@@ -61,3 +61,10 @@ def test_full_size_encode_is_bit_exact(full_runs, name):
 def test_full_size_decode_matches_oracle(full_runs, name):
     w, g, o, rng = full_runs(name)
     compare(w, g, o, rng, label="%s full size" % name)
+    if name in ("gqa_t32k", "long_t128k"):
+        # the single-tier pools again with the query direction in binary32
+        # (the precise mode, a few per cent slower on these pools)
+        from long_context_decode_ada_amd import ska
+        g32 = gpu_run(w, query_precision=ska.QDIR_F32)
+        assert g32["errors"] == 0
+        compare(w, g32, o, rng, label="%s full size, binary32 query direction" % name)
