@@ -31,7 +31,7 @@ def _case(seed):
     for s in range(B):                      # some lengths on or next to a page boundary
         if r.random() < 0.4:
             lens[s] = int(r.integers(0, 40)) * PAGE + int(r.choice([-1, 0, 1]))
-    lens = np.clip(lens, 0, None).astype(np.int32)
+    lens = (np.clip(lens, 0, None) * LEN_SCALE).astype(np.int32)
     if r.random() < 0.4:
         tiers = [int(r.choice(TIERS))]
     else:
@@ -79,8 +79,11 @@ def _case(seed):
     return w, splits, qmode, qprec
 
 
-# 40 seeds by default; SKA_RANDOM_SEEDS=<n> runs seeds 0..n-1 (a longer sweep)
+# 40 seeds by default; SKA_RANDOM_SEEDS=<n> runs seeds 0..n-1 (a longer sweep);
+# SKA_RANDOM_LEN_SCALE=<k> multiplies the drawn lengths by k (longer rows:
+# several 64-page chunks per wave and more splits)
 NSEEDS = int(os.environ.get("SKA_RANDOM_SEEDS", "40"))
+LEN_SCALE = int(os.environ.get("SKA_RANDOM_LEN_SCALE", "1"))
 
 
 @pytest.mark.parametrize("seed", range(NSEEDS))
