@@ -124,7 +124,7 @@ typedef struct {
                                  (for keys with outlier channels, whose large radii turn that
                                  into large output errors; on MI355X about 4 % slower on a
                                  pool of one tier at d = 128 with 4 query heads per KV head,
-                                 about twice as slow on a pool of mixed tiers) */
+                                 about 40 % slower on a pool of mixed tiers) */
     /* Maxima of the decode calls on this cache, fixed when it is created:
        they size the decode workspace (split partials and merge counters),
        which is allocated then and never again.  A decode call outside them

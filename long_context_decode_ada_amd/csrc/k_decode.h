@@ -249,9 +249,10 @@ __device__ __forceinline__ float fma_mix_hi(uint32_t u, float w, float acc) {
 // instructions but twice the registers ((d/4 angles) x G heads per lane):
 // at G = 4, d = 128 the kernels run at the register limit, so they extract
 // the codes without spread words (CodeAddr); single-tier pools then decode
-// about 4 % slower than with binary16 (b = 4; 1-2 % at b = 3), while the
-// header-dispatched kernel spills and runs at about half speed.  So binary16
-// is the default and binary32 the precise mode.// 32-bit words of the query direction per lane: (D/4 angles) x G heads
+// about 4 % slower than with binary16 (b = 4; 1-2 % at b = 3); the
+// header-dispatched kernel reads the query words from LDS instead
+// (slice_fb_lds) and runs about 40 % slower.  So binary16 is the default and
+// binary32 the precise mode.// 32-bit words of the query direction per lane: (D/4 angles) x G heads
 template <int D, int G, bool QF>
 constexpr int query_words() { return QF ? D * G / 4 : D * G / 8; }
 
@@ -542,6 +543,46 @@ __device__ __forceinline__ void slice_fb(const PageBuf<D> &r, const uint32_t (&u
     }
 }
 
+// The header-dispatched kernel with the binary32 direction at G = 4,
+// d = 128: its registers cannot hold the 128 query words besides everything
+// else (the compiler spilled inside the page loop and the kernel ran at half
+// speed), so the slice loop reads each angle's four heads from the
+// workgroup's LDS copy (one 16-byte read per angle; uqs = the lane's slice
+// of the tier's block, [angle][head]) instead.
+template <int D, int B>
+__device__ __forceinline__ void slice_fb_lds(const PageBuf<D> &r, const float *__restrict__ uqs,
+                                             const float2 *__restrict__ lut, float (&F)[4], float &P) {
+    constexpr int NA = D / 4;
+    const int j = threadIdx.x & 3;
+    const uint32_t az_base = 8u * ((j == 3) ? lut_azimuth(B) : lut_polar(B));
+    const uint32_t pad_base = 8u * ((j == 3) ? kLutOnes : lut_polar(B));
+    const char *lutb = reinterpret_cast<const char *>(lut);
+    CodeAddr<B, false> ca;
+    ca.init(r.cw);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) F[h] = 0.f;
+    P = 1.f;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const uint32_t c8 = ca.at(r.cw, i);
+        uint32_t e8;
+        if (i == NA - 2) e8 = az_base + c8;
+        else if (i == NA - 1) e8 = pad_base + c8;
+        else e8 = 8u * lut_polar(B) + c8;
+        const float2 cs = *reinterpret_cast<const float2 *>(lutb + e8);
+        const float4 uv = *reinterpret_cast<const float4 *>(uqs + 4 * i);
+        const float w = P * cs.x;
+        P = P * cs.y;
+        F[0] = __builtin_fmaf(uv.x, w, F[0]);
+        F[1] = __builtin_fmaf(uv.y, w, F[1]);
+        F[2] = __builtin_fmaf(uv.z, w, F[2]);
+        F[3] = __builtin_fmaf(uv.w, w, F[3]);
+    }
+}
+// (whether a kernel takes that path)
+template <int D, int G, int TB, bool QF>
+constexpr bool query_in_lds() { return TB == 0 && QF && G == 4 && D == 128; }
+
 // The rest of a coded page, the same for every tier: the four slices joined
 // into f_b, the logits, online softmax and the MFMA P.V update.  DBG also
 // stores the logits (a separate kernel variant, so that the store does not
@@ -622,7 +663,8 @@ __device__ __forceinline__ void compute_page(const DecodeArgs &A, const PageDesc
                                              int64_t head0, const uint32_t (&u)[query_words<D, G, QF>()],
                                              const uint32_t (&qd)[D / 4], float sq,
                                              const float2 *__restrict__ lut, const float *__restrict__ rlev,
-                                             float *__restrict__ pb, WaveState &st, v4f (&acc)[D / 16]) {
+                                             float *__restrict__ pb, WaveState &st, v4f (&acc)[D / 16],
+                                             const float *__restrict__ uq_all = nullptr) {
     // tokens of the page: its first slots, up to the row's length and (coded
     // pools) the header's count (the high four bits count empty slots)
     int ntok = min(kPage, len - pd.p * kPage);
@@ -645,12 +687,25 @@ __device__ __forceinline__ void compute_page(const DecodeArgs &A, const PageDesc
         // the P.V product exist once, after the dispatch
         ntok = min(ntok, pd.cnt);
         float F[G], P;
-        switch (pd.b) {
-            case 2: slice_fb<D, G, 2, QF>(r, u, lut, F, P); break;
-            case 3: slice_fb<D, G, 3, QF>(r, u, lut, F, P); break;
-            case 4: slice_fb<D, G, 4, QF>(r, u, lut, F, P); break;
-            case 6: slice_fb<D, G, 6, QF>(r, u, lut, F, P); break;
-            default: slice_fb<D, G, 8, QF>(r, u, lut, F, P); break;
+        if constexpr (query_in_lds<D, G, TB, QF>()) {
+            // the tier's block of the LDS copy: slot among the tiers present, the lane's slice
+            const int slot = __builtin_popcount(A.tier_mask & ((1u << pd.b) - 1u));
+            const float *uqs = uq_all + ((slot * 4 + (int)(threadIdx.x & 3)) * (D / 4)) * G;
+            switch (pd.b) {
+                case 2: slice_fb_lds<D, 2>(r, uqs, lut, F, P); break;
+                case 3: slice_fb_lds<D, 3>(r, uqs, lut, F, P); break;
+                case 4: slice_fb_lds<D, 4>(r, uqs, lut, F, P); break;
+                case 6: slice_fb_lds<D, 6>(r, uqs, lut, F, P); break;
+                default: slice_fb_lds<D, 8>(r, uqs, lut, F, P); break;
+            }
+        } else {
+            switch (pd.b) {
+                case 2: slice_fb<D, G, 2, QF>(r, u, lut, F, P); break;
+                case 3: slice_fb<D, G, 3, QF>(r, u, lut, F, P); break;
+                case 4: slice_fb<D, G, 4, QF>(r, u, lut, F, P); break;
+                case 6: slice_fb<D, G, 6, QF>(r, u, lut, F, P); break;
+                default: slice_fb<D, G, 8, QF>(r, u, lut, F, P); break;
+            }
         }
         finish_page<D, G, DBG>(A, r, ntok, lbase, F, P, sq, rlev, pb, st, acc);
     }
@@ -1383,8 +1438,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
             for (int i = 0; i < kBufs; ++i) {
                 if (k + i < nvalid) {
-                    ensure_query(dd[i].b);
-                    compute_page<D, G, TB, DBG, QF>(A, dd[i], R[i], len, head0, u, qd, sq, lut, rlev, pb, st, acc);
+                    if constexpr (!query_in_lds<D, G, TB, QF>()) ensure_query(dd[i].b);
+                    compute_page<D, G, TB, DBG, QF>(A, dd[i], R[i], len, head0, u, qd, sq, lut, rlev, pb, st, acc,
+                                                    reinterpret_cast<const float *>(uq_lds));
                 }
                 dd[i] = desc(min(k + i + kBufs, last));
                 dd[i].live = k + i + kBufs < nvalid;   // (past the chunk: empty descriptors, no reads)
